@@ -1,0 +1,269 @@
+"""Seeded synthetic inputs for EAGLE target-verify attention (topk = 1).
+
+This module only *draws* inputs: prefix lengths, a paged KV pool with a
+shuffled page table, and bf16 / fp8-e4m3fn encoded q, k, v.  It holds none of
+the attention arithmetic, so both the fp64 CPU oracle and the HIP path can be
+fed from it without sharing any computation.
+
+Layouts follow the paged-cache views of the pages' unified-attention call
+(PR #23146, "Code Review" excerpt: ``k_cache.view(-1, page_size, H_kv, d)``,
+``o.view(-1, H_q, v_head_dim)``):
+
+* ``q``        [B*D, H_q, qk_dim]  bf16 bits (uint16); row ``b*D + i`` is draft i of sequence b
+* ``k_cache``  [num_slots, H_kv, k_row]  bf16 bits (uint16) or e4m3fn bytes (uint8)
+* ``v_cache``  [num_slots, H_kv, v_dim]  same dtype; ``None`` when V aliases the
+  first ``v_dim`` columns of the K row (the MLA latent layout)
+* ``kv_indptr`` int32 [B+1], ``kv_indices`` int32 [sum(L_b + D)]: the token-level
+  slot list of each sequence, prefix tokens first, then its D draft tokens
+  (PR #23146, "Code Review": ``kv_indptr, kv_indices = spec_info.kv_indptr, ...``).
+  Within a page the slots are consecutive, which is what makes a page table valid
+  at topk = 1 (PR #5168, reviewer note that all tokens in the page table are
+  consecutive when top k = 1).
+
+Recipe (seed = 1000 + config index unless given; NumPy PCG64 ``default_rng``),
+drawn in this order: prefix lengths (integers, both ends inclusive), the page
+permutation, q, k, v.  Normal values are drawn as float32 and rounded to bf16
+with round-to-nearest-even; fp8 values are ``e4m3fn(x / scale)`` with RNE and
+saturation to +-448.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+KV_BF16 = 0
+KV_FP8_E4M3FN = 1
+
+# bit patterns used to poison memory that must never be read
+BF16_NAN_BITS = 0x7FC0
+E4M3FN_NAN_BITS = 0x7F
+
+
+@dataclasses.dataclass
+class Problem:
+    """One verify-attention call's inputs, all on the host."""
+
+    name: str
+    batch: int
+    draft_len: int
+    hq: int
+    hkv: int
+    qk_dim: int
+    v_dim: int
+    page_size: int
+    kv_dtype: int                 # KV_BF16 or KV_FP8_E4M3FN
+    k_scale: float
+    v_scale: float
+    sm_scale: float
+    window_left: int              # -1: no window
+    num_splits: int               # 0: library heuristic
+    prefix_lens: np.ndarray       # int32 [B]
+    kv_indptr: np.ndarray         # int32 [B+1]
+    kv_indices: np.ndarray        # int32 [sum n_b]
+    page_ids: list                # per sequence: int64 array of its page ids (in order)
+    num_pages: int                # pool size in pages
+    q: np.ndarray                 # uint16 [B*D, Hq, qk_dim]
+    k_cache: np.ndarray           # uint16 / uint8 [num_slots, Hkv, k_row]
+    v_cache: Optional[np.ndarray]  # same dtype [num_slots, Hkv, v_dim] or None (alias of K)
+    seed: int = 0
+
+    @property
+    def v_aliases_k(self) -> bool:
+        return self.v_cache is None
+
+    @property
+    def num_slots(self) -> int:
+        return self.num_pages * self.page_size
+
+    @property
+    def max_prefix_len(self) -> int:
+        return int(self.prefix_lens.max()) if self.batch else 0
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        if self.batch == 0:
+            return 1
+        return max(1, -(-(self.max_prefix_len + self.draft_len) // self.page_size))
+
+    @property
+    def elem_bytes(self) -> int:
+        return 1 if self.kv_dtype == KV_FP8_E4M3FN else 2
+
+    def v_view(self) -> np.ndarray:
+        """The V cache as an array [num_slots, Hkv, v_dim] (a view when V aliases K)."""
+        if self.v_cache is None:
+            return self.k_cache[:, :, : self.v_dim]
+        return self.v_cache
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round-to-nearest-even (torch's conversion)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _e4m3fn_bytes(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3fn bytes, RNE with saturation to +-448 (torch's conversion)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).clamp_(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _normal_encoded(rng: np.random.Generator, shape, kv_dtype: int, scale: float,
+                    chunk: int = 1 << 24) -> np.ndarray:
+    """Draw N(0,1) float32 values in order and encode them, chunk by chunk."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8 if kv_dtype == KV_FP8_E4M3FN else np.uint16)
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        x = rng.standard_normal(hi - lo, dtype=np.float32)
+        if kv_dtype == KV_FP8_E4M3FN:
+            out[lo:hi] = _e4m3fn_bytes(x / np.float32(scale))
+        else:
+            out[lo:hi] = _bf16_bits(x)
+    return out.reshape(shape)
+
+
+def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
+                 prefix_range: Optional[Sequence[int]] = None, draft_len: int = 4,
+                 hq: int, hkv: int, qk_dim: int, v_dim: Optional[int] = None,
+                 page_size: int = 1, kv_dtype: int = KV_BF16, kv_scale: float = 1.0,
+                 v_aliases_k: bool = False, sm_scale: Optional[float] = None,
+                 window_left: int = -1, num_splits: int = 0,
+                 num_pages: Optional[int] = None, pool_factor: float = 1.25,
+                 seed: int = 0, poison: bool = False) -> Problem:
+    """Draw one problem.
+
+    ``prefix_lens``: explicit list, or ``prefix_range=(lo, hi)`` for
+    uniform integers in [lo, hi].  ``num_pages`` fixes the pool size, else
+    ``ceil(pool_factor * total pages)``.  With ``poison`` the pool's page 0 is
+    reserved and every slot no sequence owns (including the unused tail of a
+    sequence's last page) holds NaN bit patterns.
+    """
+    v_dim = qk_dim if v_dim is None else v_dim
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(qk_dim)
+    rng = np.random.default_rng(seed)
+
+    # 1. prefix lengths
+    if prefix_lens is not None:
+        lens = np.asarray(prefix_lens, dtype=np.int64).reshape(batch)
+    elif prefix_range is not None:
+        lens = rng.integers(prefix_range[0], prefix_range[1] + 1, size=batch).astype(np.int64)
+    else:
+        raise ValueError("give prefix_lens or prefix_range")
+    n_tok = lens + draft_len
+    n_pages = -(-n_tok // page_size)
+    total_pages = int(n_pages.sum())
+
+    # 2. page permutation: each sequence's pages, in order, from a shuffled pool
+    reserved = 1 if poison else 0
+    if num_pages is None:
+        num_pages = max(int(math.ceil(pool_factor * total_pages)), total_pages) + reserved
+    if num_pages - reserved < total_pages:
+        raise ValueError("pool too small")
+    perm = rng.permutation(num_pages - reserved)[:total_pages] + reserved
+    page_ids = []
+    indptr = np.zeros(batch + 1, dtype=np.int64)
+    indices = np.empty(int(n_tok.sum()), dtype=np.int64)
+    off = 0
+    for b in range(batch):
+        pg = perm[off: off + n_pages[b]].astype(np.int64)
+        off += n_pages[b]
+        page_ids.append(pg)
+        t = np.arange(n_tok[b], dtype=np.int64)
+        indices[indptr[b]: indptr[b] + n_tok[b]] = pg[t // page_size] * page_size + t % page_size
+        indptr[b + 1] = indptr[b] + n_tok[b]
+
+    # 3-5. q, k, v
+    num_slots = num_pages * page_size
+    q = _normal_encoded(rng, (batch * draft_len, hq, qk_dim), KV_BF16, 1.0)
+    k = _normal_encoded(rng, (num_slots, hkv, qk_dim), kv_dtype, kv_scale)
+    v = None if v_aliases_k else _normal_encoded(rng, (num_slots, hkv, v_dim), kv_dtype, kv_scale)
+
+    if poison:
+        owned = np.zeros(num_slots, dtype=bool)
+        owned[indices] = True
+        nan = E4M3FN_NAN_BITS if kv_dtype == KV_FP8_E4M3FN else BF16_NAN_BITS
+        k[~owned] = nan
+        if v is not None:
+            v[~owned] = nan
+
+    return Problem(
+        name=name, batch=batch, draft_len=draft_len, hq=hq, hkv=hkv, qk_dim=qk_dim,
+        v_dim=v_dim, page_size=page_size, kv_dtype=kv_dtype,
+        k_scale=float(kv_scale) if kv_dtype == KV_FP8_E4M3FN else 1.0,
+        v_scale=float(kv_scale) if kv_dtype == KV_FP8_E4M3FN else 1.0,
+        sm_scale=float(sm_scale), window_left=int(window_left), num_splits=int(num_splits),
+        prefix_lens=lens.astype(np.int32), kv_indptr=indptr.astype(np.int32),
+        kv_indices=indices.astype(np.int32), page_ids=page_ids, num_pages=int(num_pages),
+        q=q, k_cache=k, v_cache=v, seed=seed)
+
+
+# The five workloads.  Shapes follow the pages' serving settings: 4 draft tokens at
+# topk = 1 (PR #5168 benchmark server flags), page sizes 1/4/16/64, head dims 128 and
+# 256 (PR #27382 accuracy tests), GQA, and an MLA latent head whose V is the first 512
+# columns of the 576-wide K row (PR #23146 review: qk_head_dim may differ from v_head_dim).
+CONFIG_NAMES = (
+    "tiny-verify",
+    "llama8b-verify",
+    "long-context-batch",
+    "sliding-window-gqa",
+    "mla-fp8-share",
+)
+
+
+def config_kwargs(idx: int) -> dict:
+    if idx == 0:
+        return dict(batch=1, prefix_lens=[256], draft_len=4, hq=8, hkv=2, qk_dim=128,
+                    page_size=1, num_pages=260, num_splits=4)
+    if idx == 1:
+        return dict(batch=4, prefix_lens=[2048] * 4, draft_len=4, hq=32, hkv=8, qk_dim=128,
+                    page_size=4, num_pages=4096)
+    if idx == 2:
+        return dict(batch=32, prefix_range=(4096, 32768), draft_len=4, hq=32, hkv=8,
+                    qk_dim=128, page_size=16)
+    if idx == 3:
+        return dict(batch=16, prefix_range=(16384, 65536), draft_len=4, hq=32, hkv=4,
+                    qk_dim=256, v_dim=256, page_size=64, window_left=4096)
+    if idx == 4:
+        return dict(batch=64, prefix_range=(1024, 8192), draft_len=4, hq=16, hkv=1,
+                    qk_dim=576, v_dim=512, v_aliases_k=True, kv_dtype=KV_FP8_E4M3FN,
+                    kv_scale=0.05, page_size=64, sm_scale=1.0 / math.sqrt(192.0))
+    raise ValueError(f"no config {idx}")
+
+
+def make_config(idx: int, seed: Optional[int] = None, **overrides) -> Problem:
+    kw = config_kwargs(idx)
+    kw.update(overrides)
+    return make_problem(name=CONFIG_NAMES[idx], seed=1000 + idx if seed is None else seed, **kw)
+
+
+def visible_token_count(prefix_len: int, draft_len: int, window_left: int) -> int:
+    """Keys that at least one of a sequence's D draft rows may see.
+
+    Row i (absolute position L+i) sees keys t <= L+i, and with a left window W only
+    t >= L+i-W (flash-attention ``window_size=(W, -1)``); the union over rows is
+    [max(0, L-W), L+D).
+    """
+    lo = 0 if window_left < 0 else max(0, prefix_len - window_left)
+    return prefix_len + draft_len - lo
+
+
+def algorithmic_kv_bytes(p: Problem) -> int:
+    """KV bytes a verify call must read: every visible token once per KV head.
+
+    K and V rows count separately unless V aliases K, in which case the K row
+    (qk_dim wide) already holds V.  Excludes q, the output, indices, partials and
+    page-rounding over-fetch.
+    """
+    per_tok = p.hkv * (p.qk_dim + (0 if p.v_aliases_k else p.v_dim)) * p.elem_bytes
+    toks = sum(visible_token_count(int(L), p.draft_len, p.window_left) for L in p.prefix_lens)
+    return int(toks) * per_tok
