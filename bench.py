@@ -1,0 +1,242 @@
+"""Benchmark: EAGLE target-verify attention (topk = 1) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--all-configs]
+
+One step = the whole path on one batch: block-table scatter, split-KV pass over
+the prefix, combine with the draft block.  Inputs are seeded synthetic workloads
+resident in HBM before timing starts.  Prints ONE JSON line:
+
+  value          KV-read GB/s of the whole step (algorithmic bytes / step time)
+  roofline       the split-KV kernel (the dominant one): algorithmic bytes per
+                 launch / its mean launch time from HIP events on its stream,
+                 against the 8 TB/s HBM peak
+  cpu_baseline   the fp64 oracle timed on a bounded sample of the same workload
+  per_config     (with --all-configs) the other large workloads, same protocol
+
+Workloads whose read set fits the 256 MB Infinity Cache are run over several
+copies of the KV pool in rotation so every step reads memory the previous steps
+did not touch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CACHE_BYTES = 256 << 20
+
+
+def prefix_kv_bytes(p) -> int:
+    """Algorithmic bytes of the split-KV launch: attended prefix tokens only (the
+    draft tokens are read by the combine)."""
+    from speculative_decoding_verify_02_amd import workloads as W
+    per_tok = p.hkv * (p.qk_dim + (0 if p.v_aliases_k else p.v_dim)) * p.elem_bytes
+    toks = sum(W.visible_token_count(int(L), 0, p.window_left) for L in p.prefix_lens)
+    return int(toks) * per_tok
+
+
+def traffic_for(workload: str, src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if recorded for this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("splitkv_fwd.hip", "va_internal.h", "verify_attn.hip"):
+        with open(os.path.join(ROOT, "speculative_decoding_verify_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
+    import torch
+
+    from speculative_decoding_verify_02_amd import binding
+    from speculative_decoding_verify_02_amd import workloads as W
+    from speculative_decoding_verify_02_amd.runner import DeviceProblem
+
+    t0 = time.time()
+    p = W.make_config(idx)
+    log(f"[bench] config {idx} {p.name}: inputs drawn in {time.time() - t0:.1f}s")
+    kv_bytes = W.algorithmic_kv_bytes(p)
+    fwd_bytes = prefix_kv_bytes(p)
+    copies = 1 if kv_bytes > 2 * CACHE_BYTES else 3
+    dp = DeviceProblem(p, device="cuda", num_splits=splits, kv_copies=copies)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for w in range(warmup):
+        dp.step(copy=w % copies)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        c = k % copies
+        e = ev[k]
+        e[0].record(stream)
+        dp.build_block_table()
+        e[1].record(stream)
+        binding.verify_attn_fwd(dp.calls[c])
+        e[2].record(stream)
+        binding.verify_attn_combine(dp.calls[c])
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    bt_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    comb_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    ms_per_step = wall * 1e3 / steps
+    rec = dict(
+        idx=idx, name=p.name, p=p, kv_bytes=kv_bytes, fwd_bytes=fwd_bytes,
+        ms_per_step=ms_per_step, bt_us=bt_ms * 1e3, fwd_us=fwd_ms * 1e3, comb_us=comb_ms * 1e3,
+        splits=dp.splits, copies=copies,
+        step_gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        fwd_gbs=fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+        kernels_gbs=kv_bytes / ((bt_ms + fwd_ms + comb_ms) * 1e-3) / 1e9,
+    )
+    log(f"[bench] config {idx}: {ms_per_step * 1e3:.1f} us/step (bt {rec['bt_us']:.1f} + fwd "
+        f"{rec['fwd_us']:.1f} + combine {rec['comb_us']:.1f} us), KV {kv_bytes / 1e6:.1f} MB, "
+        f"step {rec['step_gbs']:.0f} GB/s, fwd {rec['fwd_gbs']:.0f} GB/s "
+        f"({100 * rec['fwd_gbs'] / HBM_PEAK_GBS:.1f}% of peak), splits {dp.splits}")
+    del dp
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_baseline(p, budget_s: float = 12.0, log=print):
+    """The oracle as it stands on a bounded prefix of the workload's sequences, BLAS
+    pinned to one thread (so `cores` is exactly what ran)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from speculative_decoding_verify_02_amd import workloads as W
+
+    per_tok = p.hkv * (p.qk_dim + (0 if p.v_aliases_k else p.v_dim)) * p.elem_bytes
+    done_bytes, nseq = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(p.batch):
+            rows = list(range(b * p.draft_len, (b + 1) * p.draft_len))
+            oracle.run(p, rows=rows)
+            done_bytes += W.visible_token_count(int(p.prefix_lens[b]), p.draft_len,
+                                                p.window_left) * per_tok
+            nseq += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    log(f"[bench] cpu oracle: {nseq} of {p.batch} sequences in {dt:.1f}s")
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nseq} of {p.batch} sequences of {p.name} (all draft rows and heads), "
+                      f"{done_bytes / 1e6:.1f} MB of KV in {dt:.1f}s, fp64 NumPy, BLAS 1 thread"}
+
+
+def workload_config(p) -> dict:
+    L = p.prefix_lens
+    return {"workload": p.name, "batch": p.batch, "prefix_len_min": int(L.min()),
+            "prefix_len_max": int(L.max()), "draft_len": p.draft_len, "hq": p.hq, "hkv": p.hkv,
+            "qk_dim": p.qk_dim, "v_dim": p.v_dim, "page_size": p.page_size,
+            "kv_dtype": "fp8_e4m3fn" if p.kv_dtype == 1 else "bf16",
+            "window_left": p.window_left}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="headline workload index")
+    ap.add_argument("--all-configs", action="store_true", help="also time the other large workloads")
+    ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for "
+              f"--gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    if not name.startswith("gfx950"):
+        print(f"bench.py targets MI355X (gfx950); found {name}", file=sys.stderr)
+        sys.exit(1)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    head = measure(args.config, args.steps, args.warmup, args.splits, log)
+    per_config = {}
+    if args.all_configs:
+        for idx in (0, 1, 2, 3, 4):
+            if idx == args.config:
+                continue
+            r = measure(idx, args.steps, args.warmup, None, log)
+            per_config[r["name"]] = {
+                "us_per_step": round(r["ms_per_step"] * 1e3, 2), "fwd_us": round(r["fwd_us"], 2),
+                "combine_us": round(r["comb_us"], 2), "block_table_us": round(r["bt_us"], 2),
+                "kv_mb": round(r["kv_bytes"] / 1e6, 2),
+                "step_gbs": round(r["step_gbs"], 1), "fwd_gbs": round(r["fwd_gbs"], 1),
+                "fwd_pct_of_peak": round(100 * r["fwd_gbs"] / HBM_PEAK_GBS, 2),
+                "kernels_pct_of_peak": round(100 * r["kernels_gbs"] / HBM_PEAK_GBS, 2),
+                "splits": r["splits"], "kv_copies": r["copies"]}
+
+    src_hash = kernel_source_hash()
+    p = head["p"]
+    traffic = traffic_for(p.name, src_hash)
+    roof = {"bound": "hbm", "achieved": round(head["fwd_gbs"], 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(head["fwd_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel": "splitkv_fwd_kernel",
+            "algorithmic_bytes_per_launch": head["fwd_bytes"],
+            "mean_launch_us": round(head["fwd_us"], 2)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(p, log=log)
+
+    out = {
+        "metric": "verify-attention us/call + KV-read HBM GB/s (% of MI355X peak) at 1 GPU",
+        "value": round(head["step_gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "us_per_call": round(head["ms_per_step"] * 1e3, 2),
+        "pct_of_peak": round(100 * head["step_gbs"] / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, shuffled page table)",
+        "config": dict(workload_config(p), splits=head["splits"], kv_copies=head["copies"],
+                       kv_mb=round(head["kv_bytes"] / 1e6, 2)),
+        "kernel_us": {"block_table": round(head["bt_us"], 2), "splitkv_fwd": round(head["fwd_us"], 2),
+                      "combine": round(head["comb_us"], 2)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if per_config:
+        out["per_config"] = per_config
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

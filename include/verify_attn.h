@@ -1,0 +1,192 @@
+/*
+ * verify_attn.h - EAGLE target-verify attention at topk = 1 on MI355X (gfx950).
+ *
+ * What the library computes
+ *   Each of B sequences has a prefix of L_b tokens and D draft tokens whose K/V
+ *   already sit in a paged KV cache right after the prefix.  Draft row i of
+ *   sequence b (absolute position p = L_b + i) attends, per query head h, to the
+ *   keys t in [0, p] of its own sequence (bottom-right causal; at topk = 1 the
+ *   draft tree is a single chain so no custom mask is needed - PR #27382
+ *   "[AMD][Perf] Split-KV flash-decode attention for EAGLE target-verify",
+ *   section "Modifications"), optionally limited to t >= p - W by a left sliding
+ *   window in flash-attention's window_size=(W, -1) convention (PR #23146,
+ *   "Code Review" on the target-verify unified-attention call).
+ *
+ *   The work is split as on PR #27382 ("Motivation", "Modifications"): a
+ *   split-KV (flash-decode) pass over the prefix writes one partial output and
+ *   log-sum-exp per split (verify_attn_fwd), then a combine merges the partials
+ *   with the causal draft-draft block (verify_attn_combine).  The paged cache is
+ *   addressed through a 2-D block table built from the token-level
+ *   kv_indptr/kv_indices lists (verify_attn_build_block_table; PR #23146 builds
+ *   the same table with scatter kernels, and PR #5168 notes that at topk = 1 the
+ *   tokens of a page are consecutive, which is what makes the table valid).
+ *
+ * Conventions for every entry point
+ *   - Pointers named in a verify_attn_args or passed to build_block_table are
+ *     DEVICE pointers; the caller allocates and owns all memory.  The library
+ *     never allocates, frees or synchronises, and keeps no pointer after a call.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream).
+ *   - Every launch decision depends only on host scalars, never on device data,
+ *     so calls are safe to record into a HIP graph (workspace addresses stay fixed).
+ *   - Calls return a status; on any status other than VA_OK nothing was launched.
+ *     Device data that breaks a stated precondition (page ids outside the pool,
+ *     a block table too narrow) is NOT detected and may fault the GPU.
+ *   - Indices are int32; byte offsets are computed in 64 bits.
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define VA_OK 0           /* success                                                   */
+#define VA_EINVAL 1       /* null pointer, negative size, bad stride or alignment      */
+#define VA_EUNSUPPORTED 2 /* valid request this library does not serve: caller falls back
+                             (the static-shape gate of PR #27382, "Modifications")      */
+#define VA_EWORKSPACE 3   /* workspace smaller than verify_attn_workspace_bytes()       */
+#define VA_EHIP 4         /* the HIP runtime reported an error on launch                */
+
+/* KV cache element types */
+#define VA_KV_BF16 0          /* bfloat16                                               */
+#define VA_KV_FP8_E4M3FN 1    /* OCP fp8 e4m3fn; value = code * k_scale (or v_scale)    */
+
+/*
+ * Arguments of verify_attn_fwd / verify_attn_combine / verify_attn_can_handle.
+ * Plain C struct passed by pointer; struct_size must be sizeof(verify_attn_args).
+ * All strides are in ELEMENTS of the pointed-to type; the innermost dimension of
+ * every tensor is contiguous.  q and out are indexed by query row r = b*D + i
+ * (the uniform-draft qo_indptr of PR #23146).
+ */
+typedef struct verify_attn_args {
+    int32_t struct_size;
+
+    /* problem shape */
+    int32_t batch;          /* B >= 0                                                   */
+    int32_t draft_len;      /* D, 1..8                                                  */
+    int32_t hq, hkv;        /* query / KV heads; hq % hkv == 0, G = hq / hkv            */
+    int32_t qk_dim, v_dim;  /* (128,128), (256,256) or (576,512); v_dim may differ from
+                               qk_dim (PR #23146 review on the output view)              */
+    int32_t page_size;      /* P: a power of two, 1..1024                               */
+    int32_t kv_dtype;       /* VA_KV_BF16 or VA_KV_FP8_E4M3FN (q is always bf16)        */
+    float k_scale, v_scale; /* dequantisation multipliers of the fp8 cache (PR #27382
+                               "Modifications"); must be 1.0 for bf16                    */
+    float sm_scale;         /* softmax scale applied to q.k                             */
+    int32_t window_left;    /* -1: no window; W >= 0: keep keys t >= p - W              */
+    int32_t max_prefix_len; /* host-side upper bound of prefix_lens[b]; sizes the grid.
+                               A larger device value stays correct but runs slower.     */
+    int32_t num_splits;     /* 0: library heuristic (CU count); else split slots per
+                               (sequence, KV head), >= 1                                 */
+
+    /* q: [B*D, hq, qk_dim] bf16                                                        */
+    const void* q;
+    int64_t q_stride_row, q_stride_head;
+    /* K cache: row of token slot s, KV head g at k_cache + s*k_stride_slot +
+       g*k_stride_head, qk_dim elements; slot s = page*P + offset (the
+       [-1, P, hkv, d] paged view of PR #23146)                                         */
+    const void* k_cache;
+    int64_t k_stride_slot, k_stride_head;
+    /* V cache, same addressing, v_dim elements.  May equal k_cache with the same
+       strides (MLA: V is the first v_dim columns of the K row).                        */
+    const void* v_cache;
+    int64_t v_stride_slot, v_stride_head;
+    /* [B, max_pages_per_seq] int32 page ids, from verify_attn_build_block_table       */
+    const int32_t* block_table;
+    int32_t max_pages_per_seq;
+    /* [B] int32 prefix lengths L_b (the KV length of sequence b is L_b + D)           */
+    const int32_t* prefix_lens;
+
+    /* fp32 workspace of at least verify_attn_workspace_bytes() bytes, written by
+       verify_attn_fwd and read by verify_attn_combine                                  */
+    float* workspace;
+    int64_t workspace_bytes;
+
+    /* out: [B*D, hq, v_dim] bf16 (round to nearest even)                               */
+    void* out;
+    int64_t o_stride_row, o_stride_head;
+    /* lse: [B*D, hq] fp32 contiguous natural-log LSE of the scaled scores, or NULL     */
+    float* lse;
+} verify_attn_args;
+
+/*
+ * Block-table scatter (PR #23146 page-table scatter kernels; validity at topk = 1
+ * from PR #5168).  For sequence b with n_b = kv_indptr[b+1] - kv_indptr[b] tokens:
+ *     block_table[b*max_pages_per_seq + p] = kv_indices[kv_indptr[b] + p*P] / P
+ * for p < ceil(n_b / P), and 0 for the remaining columns.  kv_lens (optional,
+ * NULL to skip) receives n_b, the per-sequence KV length that PR #23146 derives
+ * from kv_indptr.
+ *   kv_indptr  [batch+1] int32 device, non-decreasing, kv_indptr[0] = 0
+ *   kv_indices [kv_indptr[batch]] int32 device token slots; within a sequence the
+ *              slots of one page are consecutive and each sequence starts at
+ *              offset 0 of its first page
+ *   block_table [batch, max_pages_per_seq] int32 device, written
+ *   kv_lens    [batch] int32 device or NULL
+ * Precondition: max_pages_per_seq >= ceil(n_b / P) (pages past the width are dropped).
+ * Errors: VA_EINVAL for null pointers with batch > 0, batch < 0, max_pages < 1;
+ *         VA_EUNSUPPORTED when page_size is not a power of two in 1..1024.
+ */
+int verify_attn_build_block_table(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                                  int32_t* block_table, int32_t* kv_lens, void* stream);
+
+/*
+ * Split-KV pass over the prefix (PR #27382 stage 1): for every (sequence, KV head,
+ * split) the prefix keys of the split's chunk are gathered through the block
+ * table and attended by all G*D query rows of that KV head; the split's partial
+ * output (normalised within the split, times v_scale) and its LSE go to the
+ * workspace.  Splits cut [max(0, L_b - W), L_b) (or [0, L_b) without a window)
+ * into chunks of equal size.  Draft keys are left to verify_attn_combine.
+ * Errors: VA_EINVAL / VA_EUNSUPPORTED / VA_EWORKSPACE as for can_handle plus a
+ * workspace check; VA_EHIP if the launch fails.
+ */
+int verify_attn_fwd(const verify_attn_args* args, void* stream);
+
+/*
+ * Combine (PR #27382 stage 2): per query row, the causal draft-draft block (draft
+ * keys L_b .. L_b+i, within the window) forms one more partial, and all partials
+ * are merged by log-sum-exp into out (bf16) and lse (fp32, optional).
+ * Must follow verify_attn_fwd with the same args on the same stream.
+ */
+int verify_attn_combine(const verify_attn_args* args, void* stream);
+
+/*
+ * Host-only gate (PR #27382's can_handle(): reads no device memory, so it is safe
+ * during graph capture).  Returns VA_OK when fwd/combine serve these arguments,
+ * else the status they would return (VA_EINVAL or VA_EUNSUPPORTED).  Does not
+ * check the workspace size.
+ */
+int verify_attn_can_handle(const verify_attn_args* args);
+
+/*
+ * Split slots per (sequence, KV head) that the heuristic picks for this shape on
+ * the current device (from its compute-unit count).  Host only.  Returns >= 1, or
+ * -1 on invalid input.
+ */
+int32_t verify_attn_num_splits(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
+                               int32_t v_dim, int32_t max_prefix_len, int32_t window_left);
+
+/*
+ * Workspace bytes needed for num_splits split slots (>= 1):
+ *   batch * hkv * num_splits * (hq/hkv * draft_len) * (v_dim + 1) * 4.
+ * Host only.  Returns -1 on invalid input.  Size it once for the largest batch
+ * and reuse it (PR #27382 review: scratch keyed on a stable max batch, fixed
+ * addresses for graph replay).
+ */
+int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
+                                    int32_t v_dim, int32_t num_splits);
+
+/* Text for a status code (static storage). */
+const char* verify_attn_strerror(int status);
+
+/* ABI version: bumps when verify_attn_args changes layout.  This header is version 1. */
+int32_t verify_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_ATTN_H */

@@ -1,0 +1,47 @@
+// Internal declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "verify_attn.h"
+
+namespace va {
+
+// 16-byte MFMA operand of 8 bf16 and the 4-float accumulator of a 16x16 tile.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr int kTokBlock = 32;   // prefix tokens one wave handles per main-loop step
+constexpr int kWaves = 4;       // waves per split-KV workgroup
+constexpr int kMaxRows = 128;   // G*D rows one workgroup can hold
+
+// Everything the kernels need, resolved on the host from verify_attn_args.
+struct Plan {
+  int rows;         // G * D query rows per KV head
+  int group;        // G
+  int rt;           // 16-row MFMA tiles per wave (1 or 2)
+  int nrg;          // row groups per workgroup (1, 2, 4); waves per row group = 4 / nrg
+  int lg_page;      // log2(page_size)
+  int splits;       // split slots per (sequence, KV head)
+  int chunk;        // prefix tokens per split (multiple of kTokBlock)
+  int max_leff;     // max over sequences of the attended prefix length
+  int64_t ws_o_floats;  // offset of partial LSEs in the workspace (floats)
+};
+
+// Validates args (host only) and fills the plan.  Returns a VA_ status.
+int make_plan(const verify_attn_args* a, Plan* plan);
+
+// Kernel launchers (one per translation unit).
+int launch_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int32_t batch,
+                       int lg_page, int32_t max_pages, int32_t* block_table, int32_t* kv_lens,
+                       hipStream_t stream);
+int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t stream);
+int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t stream);
+
+// Compute-unit count of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace va

@@ -1,0 +1,207 @@
+// C-ABI entry points: argument checks, the static-shape gate, split planning and
+// workspace sizing.  Every decision here reads host scalars only, so a call can be
+// captured into a HIP graph (the split-KV page's can_handle() gate and its
+// max-batch-keyed scratch follow the same rule).
+
+#include <math.h>
+#include <mutex>
+
+#include "va_internal.h"
+
+namespace va {
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dims(int qk, int v) {
+  return (qk == 128 && v == 128) || (qk == 256 && v == 256) || (qk == 576 && v == 512);
+}
+
+// Attended prefix length bound: the union of the draft rows' windows starts at
+// max(0, L - W), so at most min(L, W) prefix keys are visible.
+int max_attended_prefix(int max_prefix_len, int window_left) {
+  return window_left >= 0 ? (max_prefix_len < window_left ? max_prefix_len : window_left)
+                          : max_prefix_len;
+}
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Split heuristic.  A split is one workgroup streaming `chunk` prefix tokens of one
+// (sequence, KV head).  Workgroups are sized so the chip sees several rounds of
+// them (good balance for ragged lengths) while each still streams enough bytes
+// that its fp32 partial (rows x (v_dim+1) x 4 B, written once and read once by
+// the combine) stays a few percent of its KV bytes.
+int heuristic_splits(int batch, int hkv, int max_leff, int cus) {
+  if (max_leff <= 0) return 1;
+  const long long units = (long long)batch * hkv;
+  const long long target_wgs = 16LL * cus;
+  long long chunk = (units * max_leff + target_wgs - 1) / target_wgs;
+  if (chunk < 256) chunk = 256;
+  if (chunk > 2048) chunk = 2048;
+  chunk = round_up((int)chunk, 128);
+  int s = (int)((max_leff + chunk - 1) / chunk);
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int make_plan(const verify_attn_args* a, Plan* p) {
+  if (!a || a->struct_size != (int32_t)sizeof(verify_attn_args)) return VA_EINVAL;
+  if (a->batch < 0 || a->draft_len < 1 || a->hq < 1 || a->hkv < 1 || a->max_prefix_len < 0 ||
+      a->num_splits < 0 || a->window_left < -1 || a->max_pages_per_seq < 1)
+    return VA_EINVAL;
+  if (a->hq % a->hkv != 0) return VA_EINVAL;
+  if (!(isfinite(a->sm_scale) && isfinite(a->k_scale) && isfinite(a->v_scale)))
+    return VA_EINVAL;
+  if (a->kv_dtype != VA_KV_BF16 && a->kv_dtype != VA_KV_FP8_E4M3FN) return VA_EINVAL;
+  if (a->kv_dtype == VA_KV_BF16 && (a->k_scale != 1.0f || a->v_scale != 1.0f))
+    return VA_EINVAL;
+  if (a->draft_len > 8) return VA_EUNSUPPORTED;
+  if (!supported_dims(a->qk_dim, a->v_dim)) return VA_EUNSUPPORTED;
+  if (!is_pow2(a->page_size) || a->page_size > 1024) return VA_EUNSUPPORTED;
+  const int group = a->hq / a->hkv;
+  const int rows = group * a->draft_len;
+  if (rows > kMaxRows) return VA_EUNSUPPORTED;
+
+  if (a->batch > 0) {
+    if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->prefix_lens ||
+        !a->workspace || !a->out)
+      return VA_EINVAL;
+    const int eb = a->kv_dtype == VA_KV_FP8_E4M3FN ? 1 : 2;
+    // 16-byte vector loads of q / K / V rows need 16-byte aligned rows
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
+        !aligned16(a->workspace))
+      return VA_EINVAL;
+    if (a->q_stride_row <= 0 || a->q_stride_head <= 0 || (a->q_stride_row % 8) ||
+        (a->q_stride_head % 8))
+      return VA_EINVAL;
+    const int64_t kq = 16 / eb;
+    if (a->k_stride_slot <= 0 || a->k_stride_head <= 0 || (a->k_stride_slot % kq) ||
+        (a->k_stride_head % kq) || a->v_stride_slot <= 0 || a->v_stride_head <= 0 ||
+        (a->v_stride_slot % kq) || (a->v_stride_head % kq))
+      return VA_EINVAL;
+    if (a->o_stride_row <= 0 || a->o_stride_head <= 0) return VA_EINVAL;
+    if (a->k_stride_head < a->qk_dim || a->v_stride_head < a->v_dim) return VA_EINVAL;
+  }
+
+  p->group = group;
+  p->rows = rows;
+  p->rt = (rows <= 16) ? 1 : (a->v_dim <= 256 ? 2 : 1);
+  const int tiles = (rows + 15) / 16;
+  const int groups = (tiles + p->rt - 1) / p->rt;
+  p->nrg = groups <= 1 ? 1 : (groups <= 2 ? 2 : (groups <= 4 ? 4 : 0));
+  if (p->nrg == 0) return VA_EUNSUPPORTED;
+  p->lg_page = ilog2(a->page_size);
+  p->max_leff = max_attended_prefix(a->max_prefix_len, a->window_left);
+  p->splits = a->num_splits > 0
+                  ? a->num_splits
+                  : heuristic_splits(a->batch, a->hkv, p->max_leff, device_cu_count());
+  p->chunk = p->max_leff > 0 ? round_up((p->max_leff + p->splits - 1) / p->splits, kTokBlock)
+                             : kTokBlock;
+  p->ws_o_floats = (int64_t)a->batch * a->hkv * p->splits * rows * a->v_dim;
+  return VA_OK;
+}
+
+}  // namespace va
+
+extern "C" {
+
+int32_t verify_attn_abi_version(void) { return 1; }
+
+const char* verify_attn_strerror(int status) {
+  switch (status) {
+    case VA_OK: return "ok";
+    case VA_EINVAL: return "invalid argument";
+    case VA_EUNSUPPORTED: return "unsupported shape or dtype (caller should fall back)";
+    case VA_EWORKSPACE: return "workspace too small";
+    case VA_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
+                                    int32_t v_dim, int32_t num_splits) {
+  if (batch < 0 || hkv < 1 || hq < 1 || hq % hkv || draft_len < 1 || v_dim < 1 || num_splits < 1)
+    return -1;
+  const int64_t rows = (int64_t)(hq / hkv) * draft_len;
+  return (int64_t)batch * hkv * num_splits * rows * ((int64_t)v_dim + 1) * 4;
+}
+
+int32_t verify_attn_num_splits(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
+                               int32_t v_dim, int32_t max_prefix_len, int32_t window_left) {
+  if (batch < 0 || hkv < 1 || hq < 1 || hq % hkv || draft_len < 1 || v_dim < 1 ||
+      max_prefix_len < 0 || window_left < -1)
+    return -1;
+  return va::heuristic_splits(batch, hkv, va::max_attended_prefix(max_prefix_len, window_left),
+                              va::device_cu_count());
+}
+
+int verify_attn_can_handle(const verify_attn_args* args) {
+  va::Plan p;
+  return va::make_plan(args, &p);
+}
+
+static int check_workspace(const verify_attn_args* a, const va::Plan& p) {
+  const int64_t need = verify_attn_workspace_bytes(a->batch, a->hkv, a->hq, a->draft_len,
+                                                   a->v_dim, p.splits);
+  return (need < 0 || a->workspace_bytes < need) ? VA_EWORKSPACE : VA_OK;
+}
+
+int verify_attn_fwd(const verify_attn_args* args, void* stream) {
+  va::Plan p;
+  int st = va::make_plan(args, &p);
+  if (st != VA_OK) return st;
+  if ((st = check_workspace(args, p)) != VA_OK) return st;
+  // launched even when the host bound says no prefix is attended: a device length
+  // above the bound must still be covered (the last split absorbs it)
+  if (args->batch == 0) return VA_OK;
+  return va::launch_splitkv_fwd(args, p, reinterpret_cast<hipStream_t>(stream));
+}
+
+int verify_attn_combine(const verify_attn_args* args, void* stream) {
+  va::Plan p;
+  int st = va::make_plan(args, &p);
+  if (st != VA_OK) return st;
+  if ((st = check_workspace(args, p)) != VA_OK) return st;
+  if (args->batch == 0) return VA_OK;
+  return va::launch_combine(args, p, reinterpret_cast<hipStream_t>(stream));
+}
+
+int verify_attn_build_block_table(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  int32_t batch, int32_t page_size, int32_t max_pages_per_seq,
+                                  int32_t* block_table, int32_t* kv_lens, void* stream) {
+  if (batch < 0 || max_pages_per_seq < 1) return VA_EINVAL;
+  if (!va::is_pow2(page_size) || page_size > 1024) return VA_EUNSUPPORTED;
+  if (batch == 0) return VA_OK;
+  if (!kv_indptr || !kv_indices || !block_table) return VA_EINVAL;
+  return va::launch_block_table(kv_indptr, kv_indices, batch, va::ilog2(page_size),
+                                max_pages_per_seq, block_table, kv_lens,
+                                reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -20,11 +20,15 @@ Layouts follow the paged-cache views of the pages' unified-attention call
   at topk = 1 (PR #5168, reviewer note that all tokens in the page table are
   consecutive when top k = 1).
 
-Recipe (seed = 1000 + config index unless given; NumPy PCG64 ``default_rng``),
-drawn in this order: prefix lengths (integers, both ends inclusive), the page
-permutation, q, k, v.  Normal values are drawn as float32 and rounded to bf16
-with round-to-nearest-even; fp8 values are ``e4m3fn(x / scale)`` with RNE and
-saturation to +-448.
+Recipe (seed = 1000 + config index unless given).  ``SeedSequence(seed)`` spawns
+four children: child 0 draws the prefix lengths (integers, both ends inclusive)
+and then the page permutation; child 1 draws q; children 2 and 3 draw the K and
+V pools.  Normal values are float64 N(0,1) draws made in chunks of 2^22 values,
+chunk c from its own PCG64 stream (the c-th spawn of the tensor's child), so
+chunks can be drawn in parallel; they are rounded to bf16 with
+round-to-nearest-even, or stored as ``e4m3fn(x / scale)`` with RNE and
+saturation to +-448.  Only pages some sequence owns are drawn (in page-id
+order); the rest of the pool is zero, or NaN bit patterns in poison mode.
 """
 
 from __future__ import annotations
@@ -101,34 +105,49 @@ class Problem:
 
 
 def _bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round-to-nearest-even (torch's conversion)."""
-    import torch
-
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    """float -> bf16 bit patterns with round-to-nearest-even (inputs are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    u = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 def _e4m3fn_bytes(x: np.ndarray) -> np.ndarray:
-    """float32 -> OCP e4m3fn bytes, RNE with saturation to +-448 (torch's conversion)."""
+    """float -> OCP e4m3fn bytes, RNE with saturation to +-448 (torch's conversion)."""
     import torch
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).clamp_(-448.0, 448.0)
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def _normal_encoded(rng: np.random.Generator, shape, kv_dtype: int, scale: float,
-                    chunk: int = 1 << 24) -> np.ndarray:
-    """Draw N(0,1) float32 values in order and encode them, chunk by chunk."""
-    n = int(np.prod(shape))
+_CHUNK = 1 << 22
+
+
+def _normal_encoded(seq: np.random.SeedSequence, n: int, kv_dtype: int,
+                    scale: float) -> np.ndarray:
+    """n N(0,1) values, encoded; chunk c of 2^22 values comes from spawn c of ``seq``."""
+    from concurrent.futures import ThreadPoolExecutor
+
     out = np.empty(n, dtype=np.uint8 if kv_dtype == KV_FP8_E4M3FN else np.uint16)
-    for lo in range(0, n, chunk):
-        hi = min(n, lo + chunk)
-        x = rng.standard_normal(hi - lo, dtype=np.float32)
+    nchunks = -(-n // _CHUNK)
+    kids = seq.spawn(nchunks)
+
+    def draw(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        x = np.random.default_rng(kids[c]).standard_normal(hi - lo)
         if kv_dtype == KV_FP8_E4M3FN:
-            out[lo:hi] = _e4m3fn_bytes(x / np.float32(scale))
+            out[lo:hi] = _e4m3fn_bytes(x / scale)
         else:
             out[lo:hi] = _bf16_bits(x)
-    return out.reshape(shape)
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            draw(c)
+    else:
+        import os
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), nchunks))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(draw, range(nchunks)))
+    return out
 
 
 def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
@@ -150,7 +169,8 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
     v_dim = qk_dim if v_dim is None else v_dim
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(qk_dim)
-    rng = np.random.default_rng(seed)
+    kids = np.random.SeedSequence(seed).spawn(4)
+    rng = np.random.default_rng(kids[0])
 
     # 1. prefix lengths
     if prefix_lens is not None:
@@ -182,11 +202,22 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
         indices[indptr[b]: indptr[b] + n_tok[b]] = pg[t // page_size] * page_size + t % page_size
         indptr[b + 1] = indptr[b] + n_tok[b]
 
-    # 3-5. q, k, v
+    # 3-5. q, then the owned pages of the K and V pools (in page-id order)
     num_slots = num_pages * page_size
-    q = _normal_encoded(rng, (batch * draft_len, hq, qk_dim), KV_BF16, 1.0)
-    k = _normal_encoded(rng, (num_slots, hkv, qk_dim), kv_dtype, kv_scale)
-    v = None if v_aliases_k else _normal_encoded(rng, (num_slots, hkv, v_dim), kv_dtype, kv_scale)
+    q = _normal_encoded(kids[1], batch * draft_len * hq * qk_dim, KV_BF16, 1.0)
+    q = q.reshape(batch * draft_len, hq, qk_dim)
+    owned_pages = np.sort(perm)
+
+    def pool(seq, width):
+        per_page = page_size * hkv * width
+        dt = np.uint8 if kv_dtype == KV_FP8_E4M3FN else np.uint16
+        arr = np.zeros((num_pages, per_page), dtype=dt)
+        arr[owned_pages] = _normal_encoded(seq, total_pages * per_page, kv_dtype,
+                                           kv_scale).reshape(total_pages, per_page)
+        return arr.reshape(num_slots, hkv, width)
+
+    k = pool(kids[2], qk_dim)
+    v = None if v_aliases_k else pool(kids[3], v_dim)
 
     if poison:
         owned = np.zeros(num_slots, dtype=bool)

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (elementwise |gpu - ref| <= atol + rtol*|ref|, atol = rtol):
+  bf16 output 1e-2, output with fp8 KV 3e-2, fp32 LSE 1e-3; block table bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_verify_02_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {W.KV_BF16: 1e-2, W.KV_FP8_E4M3FN: 3e-2}
+LSE_TOL = 1e-3
+
+
+def run_device(p, num_splits=None, max_prefix_len=None):
+    import torch
+    from speculative_decoding_verify_02_amd.runner import DeviceProblem
+
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    dp = DeviceProblem(p, num_splits=num_splits)
+    if max_prefix_len is not None:
+        for c in dp.calls:
+            c.args.max_prefix_len = max_prefix_len
+    dp.step()
+    return dp, dp.results()
+
+
+def describe(p, **kw):
+    extra = " ".join(f"{k}={v}" for k, v in kw.items())
+    return (f"[case] {p.name} seed={p.seed} B={p.batch} L={list(p.prefix_lens[:8])} D={p.draft_len} "
+            f"hq={p.hq} hkv={p.hkv} dk={p.qk_dim} dv={p.v_dim} P={p.page_size} "
+            f"dtype={p.kv_dtype} W={p.window_left} {extra}")
+
+
+def check(p, num_splits=None, rows=None, max_prefix_len=None, label=""):
+    print(describe(p, splits=num_splits, label=label), flush=True)
+    dp, (bt, lens, O, LSE) = run_device(p, num_splits, max_prefix_len)
+    bt_ref, lens_ref = oracle.run_block_table(p)
+    assert np.array_equal(bt, bt_ref), "block table"
+    assert np.array_equal(lens, lens_ref), "kv_lens"
+    O_ref, LSE_ref = oracle.run(p, rows=rows)
+    if rows is not None:
+        O, LSE = O[rows], LSE[rows]
+        O_ref, LSE_ref = O_ref[rows], LSE_ref[rows]
+    tol = O_TOL[p.kv_dtype]
+    ok_o, err_o, _ = oracle.allclose_report(O, O_ref, tol, tol)
+    ok_l, err_l, _ = oracle.allclose_report(LSE, LSE_ref, LSE_TOL, LSE_TOL)
+    rel = np.linalg.norm(O - O_ref) / max(np.linalg.norm(O_ref), 1e-30)
+    print(f"   max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} rel-norm(O)={rel:.3e} splits={dp.splits}",
+          flush=True)
+    assert np.isfinite(O).all() and np.isfinite(LSE).all()
+    assert ok_o, f"O mismatch (max abs {err_o})"
+    assert ok_l, f"LSE mismatch (max abs {err_l})"
+    return dp, O, LSE
+
+
+def sample_rows(p, nseq=4):
+    L = p.prefix_lens
+    seqs = sorted({0, p.batch - 1, int(np.argmin(L)), int(np.argmax(L))})[:nseq]
+    return [b * p.draft_len + i for b in seqs for i in range(p.draft_len)]
+
+
+# ---------------------------------------------------------------------------
+# the five workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_small_configs_full(idx):
+    check(W.make_config(idx), label=W.CONFIG_NAMES[idx])
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_large_configs_sampled(idx):
+    p = W.make_config(idx)
+    check(p, rows=sample_rows(p), label=W.CONFIG_NAMES[idx])
+
+
+# ---------------------------------------------------------------------------
+# shapes at sizes the oracle finishes quickly: several tiles and ragged tails
+# ---------------------------------------------------------------------------
+
+DIMS = [
+    dict(qk_dim=128, v_dim=128),
+    dict(qk_dim=256, v_dim=256),
+    dict(qk_dim=576, v_dim=512, v_aliases_k=True, kv_dtype=W.KV_FP8_E4M3FN, kv_scale=0.05,
+         sm_scale=1 / math.sqrt(192.0)),
+    dict(qk_dim=128, v_dim=128, kv_dtype=W.KV_FP8_E4M3FN, kv_scale=0.05),
+    dict(qk_dim=256, v_dim=256, kv_dtype=W.KV_FP8_E4M3FN, kv_scale=0.05),
+    dict(qk_dim=576, v_dim=512, v_aliases_k=True),
+]
+
+
+@pytest.mark.parametrize("dims", range(len(DIMS)))
+def test_edge_prefix_lengths(dims):
+    hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
+    p = W.make_problem(name="edge-lengths", batch=8, prefix_lens=[0, 1, 5, 63, 64, 65, 97, 700],
+                       hq=hq, hkv=hkv, page_size=16, seed=100 + dims, **DIMS[dims])
+    check(p, num_splits=3)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 0])
+def test_split_counts(splits):
+    p = W.make_problem(name="splits", batch=3, prefix_lens=[300, 1000, 33], hq=8, hkv=2,
+                       qk_dim=128, page_size=4, seed=200 + splits)
+    check(p, num_splits=splits)
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 4, 17, 256, 5000])
+@pytest.mark.parametrize("dims", [0, 1, 2])
+def test_windows(window, dims):
+    hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
+    p = W.make_problem(name="window", batch=4, prefix_lens=[0, 3, 700, 2000], hq=hq, hkv=hkv,
+                       page_size=64, window_left=window, seed=300 + window + dims, **DIMS[dims])
+    check(p, num_splits=3)
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_page_sizes(page_size):
+    p = W.make_problem(name="pages", batch=3, prefix_lens=[129, 513, 40], hq=8, hkv=2,
+                       qk_dim=128, page_size=page_size, seed=400 + page_size)
+    check(p, num_splits=2)
+
+
+@pytest.mark.parametrize("hq,hkv,draft", [(4, 4, 4), (8, 1, 4), (16, 2, 4), (32, 2, 2),
+                                          (32, 2, 4), (64, 2, 4), (8, 8, 1), (6, 2, 3),
+                                          (16, 2, 8)])
+def test_gqa_ratios_and_draft_lengths(hq, hkv, draft):
+    p = W.make_problem(name="gqa", batch=3, prefix_lens=[77, 400, 1], draft_len=draft, hq=hq,
+                       hkv=hkv, qk_dim=128, page_size=16, seed=500 + hq + hkv + draft)
+    check(p, num_splits=2)
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2])
+def test_poisoned_pool_is_never_read(dims):
+    hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
+    p = W.make_problem(name="poison", batch=4, prefix_lens=[0, 10, 333, 1100], hq=hq, hkv=hkv,
+                       page_size=16, poison=True, seed=600 + dims, **DIMS[dims])
+    check(p, num_splits=4)
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2])
+def test_sharp_softmax_and_planted_keys(dims):
+    hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
+    p = W.make_problem(name="sharp", batch=3, prefix_lens=[900, 50, 2048], hq=hq, hkv=hkv,
+                       page_size=16, seed=700 + dims, **DIMS[dims])
+    # sharpen every query 4x (exact in bf16: exponent shift)
+    q = p.q.astype(np.uint32)
+    exp = (q >> 7) & 0xFF
+    p.q = np.where((exp > 0) & (exp < 253), q + (2 << 7), q).astype(np.uint16)
+    # plant a key equal to a scaled copy of query (b=0, i=2, head 0) at prefix position 123
+    from speculative_decoding_verify_02_amd.workloads import _bf16_bits, _e4m3fn_bytes
+    qf = oracle.bf16_to_f64(p.q[2, 0, :p.qk_dim])
+    slot = int(p.kv_indices[p.kv_indptr[0] + 123])
+    if p.kv_dtype == W.KV_FP8_E4M3FN:
+        p.k_cache[slot, 0, :p.qk_dim] = _e4m3fn_bytes(np.clip(qf, -3, 3) / p.k_scale)
+    else:
+        p.k_cache[slot, 0, :p.qk_dim] = _bf16_bits(qf * 0.5)
+    check(p, num_splits=3)
+
+
+def test_max_prefix_hint_too_small_stays_correct():
+    p = W.make_problem(name="hint", batch=3, prefix_lens=[300, 1500, 40], hq=8, hkv=2,
+                       qk_dim=128, page_size=16, seed=800)
+    check(p, num_splits=2, max_prefix_len=200)
+
+
+def test_run_to_run_bitwise_identical():
+    p = W.make_problem(name="determinism", batch=4, prefix_lens=[3000, 17, 900, 4096], hq=32,
+                       hkv=8, qk_dim=128, page_size=16, seed=900)
+    from speculative_decoding_verify_02_amd.runner import DeviceProblem
+    print(describe(p), flush=True)
+    dp = DeviceProblem(p, num_splits=0)
+    dp.step()
+    _, _, O1, L1 = dp.results()
+    for _ in range(3):
+        dp.step()
+        _, _, O2, L2 = dp.results()
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_strided_q_and_out():
+    """q and out as views with padded head strides (the ABI takes element strides)."""
+    import torch
+    from speculative_decoding_verify_02_amd import binding as B
+    p = W.make_problem(name="strided", batch=2, prefix_lens=[100, 260], hq=8, hkv=2, qk_dim=128,
+                       page_size=4, seed=1000)
+    print(describe(p), flush=True)
+    dev = "cuda"
+    qfull = torch.zeros((p.batch * p.draft_len, p.hq, 256), dtype=torch.bfloat16, device=dev)
+    qfull[:, :, :128] = torch.from_numpy(p.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = qfull[:, :, :128]
+    k = torch.from_numpy(p.k_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+    v = torch.from_numpy(p.v_cache.view(np.int16)).view(torch.bfloat16).to(dev)
+    indptr = torch.from_numpy(p.kv_indptr).to(dev)
+    indices = torch.from_numpy(p.kv_indices).to(dev)
+    bt, _ = B.verify_attn_build_block_table(indptr, indices, p.page_size, p.max_pages_per_seq)
+    lens = torch.from_numpy(p.prefix_lens).to(dev)
+    ofull = torch.zeros((p.batch * p.draft_len, p.hq, 384), dtype=torch.bfloat16, device=dev)
+    out = ofull[:, :, 128:256]
+    ns = 2
+    ws = torch.empty(B.verify_attn_workspace_bytes(p.batch, p.hkv, p.hq, p.draft_len, 128, ns) // 4,
+                     dtype=torch.float32, device=dev)
+    call = B.make_args(q=q, k_cache=k, v_cache=v, block_table=bt, prefix_lens=lens,
+                       draft_len=p.draft_len, page_size=p.page_size, sm_scale=p.sm_scale,
+                       max_prefix_len=p.max_prefix_len, out=out, workspace=ws, num_splits=ns)
+    B.verify_attn_fwd(call)
+    B.verify_attn_combine(call)
+    torch.cuda.synchronize()
+    O = out.float().cpu().numpy().astype(np.float64)
+    O_ref, _ = oracle.run(p)
+    ok, err, _ = oracle.allclose_report(O, O_ref, 1e-2, 1e-2)
+    assert ok, err
+    assert (ofull[:, :, :128] == 0).all() and (ofull[:, :, 256:] == 0).all()
+
+
+def test_empty_batch_and_workspace_error():
+    import torch
+    from speculative_decoding_verify_02_amd import binding as B
+    p = W.make_problem(name="ws", batch=2, prefix_lens=[100, 260], hq=8, hkv=2, qk_dim=128,
+                       page_size=4, seed=1001)
+    print(describe(p), flush=True)
+    from speculative_decoding_verify_02_amd.runner import DeviceProblem
+    dp = DeviceProblem(p, num_splits=2)
+    call = dp.calls[0]
+    call.args.workspace_bytes = 16
+    assert B.verify_attn_fwd(call, check=False) == B.VA_EWORKSPACE
+    assert B.verify_attn_combine(call, check=False) == B.VA_EWORKSPACE
+    torch.cuda.synchronize()
