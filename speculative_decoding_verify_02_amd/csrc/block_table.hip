@@ -10,12 +10,20 @@
 
 namespace va {
 
-__global__ __launch_bounds__(256) void block_table_kernel(const int32_t* __restrict__ kv_indptr,
-                                                          const int32_t* __restrict__ kv_indices,
-                                                          int32_t batch, int lg_page,
-                                                          int32_t max_pages,
-                                                          int32_t* __restrict__ block_table,
-                                                          int32_t* __restrict__ kv_lens) {
+struct BlockTableParams {
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int32_t batch, lg_page, max_pages;
+  int32_t* block_table;
+  int32_t* kv_lens;
+};
+
+__global__ __launch_bounds__(256) void block_table_kernel(BlockTableParams P) {
+  const int32_t* __restrict__ kv_indptr = P.kv_indptr;
+  const int32_t* __restrict__ kv_indices = P.kv_indices;
+  const int32_t batch = P.batch, lg_page = P.lg_page, max_pages = P.max_pages;
+  int32_t* __restrict__ block_table = P.block_table;
+  int32_t* __restrict__ kv_lens = P.kv_lens;
   const int b = blockIdx.y;
   const int pg = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch || pg >= max_pages) return;
@@ -33,9 +41,9 @@ int launch_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int3
                        hipStream_t stream) {
   if (batch > 65535) return VA_EUNSUPPORTED;
   dim3 grid((max_pages + 255) / 256, batch);
-  hipLaunchKernelGGL(block_table_kernel, grid, dim3(256), 0, stream, kv_indptr, kv_indices,
-                     batch, lg_page, max_pages, block_table, kv_lens);
-  return hipGetLastError() == hipSuccess ? VA_OK : VA_EHIP;
+  const BlockTableParams p{kv_indptr, kv_indices, batch, lg_page, max_pages, block_table, kv_lens};
+  return launch_kernel(reinterpret_cast<const void*>(&block_table_kernel), grid, dim3(256), p,
+                       stream);
 }
 
 }  // namespace va

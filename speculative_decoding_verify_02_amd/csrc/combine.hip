@@ -2,8 +2,8 @@
 // stage merges the prefix splits by log-sum-exp and adds the small causal
 // draft-draft block).
 //
-// Workgroup = (KV head g, sequence b); each wave takes query rows in turn.  Per row
-// (draft i, q head h):
+// One wave per query row (draft i, q head h), lanes across the row's columns; a
+// workgroup holds 4 rows of one (sequence b, KV head g).  Per row:
 //   draft block: keys L+j for j <= i (and j >= i - W with a left window W), scores
 //   in fp32 from the bf16 q and the (dequantised) cached draft keys, softmax over
 //   them -> one more (O, LSE) partial;
@@ -72,16 +72,25 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
 }  // namespace
 
+// One wave per query row (draft i, q head h of KV head g, sequence b); lanes span
+// the row's columns.  Workgroup = 4 consecutive rows of one (b, g).
 template <int DK, int DV, bool FP8>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   constexpr int DPL = DK / 64;  // q/k elements per lane in a dot product
   constexpr int CPT = DV / 64;  // output columns per lane
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  if (row >= P.rows) return;  // no barriers in this kernel
 
   const int L = P.prefix_lens[b];
   const int lo = P.window >= 0 ? max(0, L - P.window) : 0;
@@ -90,79 +99,98 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
+  const int i = row / P.group;
+  const int h = g * P.group + row % P.group;
+  const int r = b * P.draft + i;
+  const int64_t split0 = ((int64_t)b * P.hkv + g) * P.splits;
 
-  const uint8_t* krow[8];
+  // a6: draft-draft block, keys L+jj for jj <= i inside the window (never empty)
+  float qv[DPL];
+  const uint16_t* qp =
+      reinterpret_cast<const uint16_t*>(P.q + (int64_t)r * P.q_srow + (int64_t)h * P.q_shead);
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) qv[k] = bf16_bits_to_f32(qp[lane * DPL + k]);
+  const int jlo = P.window >= 0 ? max(0, i - P.window) : 0;
+  float sc[8];
   const uint8_t* vrow[8];
-  for (int jj = 0; jj < P.draft; ++jj) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    sc[jj] = -INFINITY;
+    vrow[jj] = nullptr;
+    if (jj < jlo || jj > i) continue;
     const int t = L + jj;
     const int64_t slot = ((int64_t)bt_row[t >> lg] << lg) | (int64_t)(t & pmask);
-    krow[jj] = P.k + slot * P.k_sslot + (int64_t)g * P.k_shead;
+    const uint8_t* kr = P.k + slot * P.k_sslot + (int64_t)g * P.k_shead;
     vrow[jj] = P.v + slot * P.v_sslot + (int64_t)g * P.v_shead;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc += qv[k] * load_elem<FP8>(kr, lane * DPL + k);
+    sc[jj] = wave_sum(acc) * P.c_nat;
+    mx = fmaxf(mx, sc[jj]);
   }
-  const int64_t split0 = ((int64_t)b * P.hkv + g) * P.splits;
-  const int hq = P.hkv * P.group;
-
-  for (int row = wave; row < P.rows; row += kWaves) {
-    const int i = row / P.group;
-    const int h = g * P.group + row % P.group;
-    const int r = b * P.draft + i;
-
-    // a6: draft-draft block
-    float qv[DPL];
-    const uint16_t* qp =
-        reinterpret_cast<const uint16_t*>(P.q + (int64_t)r * P.q_srow + (int64_t)h * P.q_shead);
+  float od[CPT];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) qv[k] = bf16_bits_to_f32(qp[lane * DPL + k]);
-    float sc[8];
-    float mx = -INFINITY;
-    for (int jj = 0; jj < P.draft; ++jj) {
-      const bool vis = jj <= i && (P.window < 0 || jj >= i - P.window);
-      float sv = -INFINITY;
-      if (vis) {
-        float acc = 0.f;
+  for (int c = 0; c < CPT; ++c) od[c] = 0.f;
+  float zd = 0.f;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) acc += qv[k] * load_elem<FP8>(krow[jj], lane * DPL + k);
-        sv = wave_sum(acc) * P.c_nat;
+  for (int jj = 0; jj < 8; ++jj) {
+    if (vrow[jj] == nullptr) continue;
+    const float w = expf(sc[jj] - mx);
+    zd += w;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) od[c] += w * load_elem<FP8>(vrow[jj], lane * CPT + c);
+  }
+  const float lse_d = mx + logf(zd);
+
+  // a7: log-sum-exp merge.  Lane s holds split s's LSE (64 splits per pass).
+  const float* plse = P.part_lse + split0 * P.rows + row;
+  float M = lse_d;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const float ls = (s0 + lane < nsplit) ? plse[(int64_t)(s0 + lane) * P.rows] : -INFINITY;
+    M = fmaxf(M, wave_max(ls));
+  }
+  const float wd = expf(lse_d - M);
+  float acc[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) acc[c] = wd * od[c] * (P.v_scale / zd);
+  float Z = wd;
+  const float* po = P.part_o + (split0 * P.rows + row) * DV + lane * CPT;
+  const int64_t pstride = (int64_t)P.rows * DV;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const float ls = (s0 + lane < nsplit) ? plse[(int64_t)(s0 + lane) * P.rows] : -INFINITY;
+    const float w = (ls == -INFINITY) ? 0.f : expf(ls - M);
+    Z += wave_sum(w);
+    const int cnt = min(64, nsplit - s0);
+    int s = 0;
+    for (; s + 4 <= cnt; s += 4) {
+      float ws[4];
+      float vals[4][CPT];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ws[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+        const float* p = po + (int64_t)(s0 + s + u) * pstride;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vals[u][c] = p[c];
       }
-      sc[jj] = sv;
-      mx = fmaxf(mx, sv);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] += ws[u] * vals[u][c];
+      }
     }
-    float od[CPT];
+    for (; s < cnt; ++s) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+      const float* p = po + (int64_t)(s0 + s) * pstride;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) od[c] = 0.f;
-    float zd = 0.f;
-    for (int jj = 0; jj < P.draft; ++jj) {
-      if (sc[jj] == -INFINITY) continue;
-      const float w = expf(sc[jj] - mx);
-      zd += w;
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) od[c] += w * load_elem<FP8>(vrow[jj], lane * CPT + c);
+      for (int c = 0; c < CPT; ++c) acc[c] += wu * p[c];
     }
-    const float lse_d = mx + logf(zd);
-
-    // a7: log-sum-exp merge with the prefix splits
-    float M = lse_d;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P.part_lse[(split0 + s) * P.rows + row]);
-    const float wd = expf(lse_d - M);
-    float acc[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] = wd * od[c] * (P.v_scale / zd);
-    float Z = wd;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ls = P.part_lse[(split0 + s) * P.rows + row];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - M);
-      Z += w;
-      const float* po = P.part_o + ((split0 + s) * P.rows + row) * DV + lane * CPT;
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] += w * po[c];
-    }
-    const float invZ = 1.f / Z;
-    uint16_t* op = P.out + (int64_t)r * P.o_srow + (int64_t)h * P.o_shead + lane * CPT;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) op[c] = f32_to_bf16_rne(acc[c] * invZ);
-    if (P.lse && lane == 0) P.lse[(int64_t)r * hq + h] = M + logf(Z);
   }
+  const float invZ = 1.f / Z;
+  uint16_t* op = P.out + (int64_t)r * P.o_srow + (int64_t)h * P.o_shead + lane * CPT;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) op[c] = f32_to_bf16_rne(acc[c] * invZ);
+  if (P.lse && lane == 0) P.lse[(int64_t)r * (P.hkv * P.group) + h] = M + logf(Z);
 }
 
 int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
@@ -197,16 +225,16 @@ int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
   cp.chunk = p.chunk;
   cp.c_nat = a->sm_scale * a->k_scale;
   cp.v_scale = a->v_scale;
-  const dim3 grid(a->hkv, a->batch);
+  const dim3 grid((p.rows + kWaves - 1) / kWaves, a->hkv, a->batch);
   const bool f8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
 #define VA_LAUNCH(DK_, DV_, F8_) \
-  hipLaunchKernelGGL((combine_kernel<DK_, DV_, F8_>), grid, dim3(256), 0, st, cp)
+  return launch_kernel(reinterpret_cast<const void*>(&combine_kernel<DK_, DV_, F8_>), grid, \
+                       dim3(256), cp, st)
   if (a->qk_dim == 128) { if (f8) VA_LAUNCH(128, 128, true); else VA_LAUNCH(128, 128, false); }
   else if (a->qk_dim == 256) { if (f8) VA_LAUNCH(256, 256, true); else VA_LAUNCH(256, 256, false); }
   else if (a->qk_dim == 576) { if (f8) VA_LAUNCH(576, 512, true); else VA_LAUNCH(576, 512, false); }
-  else return VA_EUNSUPPORTED;
 #undef VA_LAUNCH
-  return hipGetLastError() == hipSuccess ? VA_OK : VA_EHIP;
+  return VA_EUNSUPPORTED;
 }
 
 }  // namespace va

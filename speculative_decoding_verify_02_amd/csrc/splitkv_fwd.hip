@@ -5,25 +5,30 @@
 // parallel programs, each writing a partial output and log-sum-exp that a second
 // stage merges.  This is the gfx950 design of that first stage:
 //
-//   workgroup = (split s, KV head g, sequence b), 4 waves of 64 lanes.
-//   All G*D query rows of KV head g form the dense M dimension (16/32/64 rows).
-//   The rows are cut into NRG row groups of 16*RT rows; the 4/NRG waves of a row
-//   group interleave the split's 32-token blocks.
+//   workgroup = (head group, split s, sequence b), 4 waves of 64 lanes.
+//   All G*D query rows of a KV head form the dense M dimension (16/32/64 rows).
+//   The 4 waves cover HPC KV heads x NRG row groups (16*RT rows each) x NTL token
+//   lanes; token lanes of one (head, row group) interleave the split's blocks and
+//   merge through LDS at the end.  The grid runs head groups fastest, so the heads
+//   of one token range are read at about the same time (DRAM locality).
 //
-// Per 32-token block a wave
-//   1. maps each token to its slot through the block table (page = bt[t >> lgP]),
-//   2. loads K rows straight into MFMA A-operand registers (lane l: token l%16,
-//      16 contiguous bytes of the row; four lanes cover 64 B of one row),
-//   3. loads V rows coalesced (16 lanes read one full row) for 8 tokens per lane,
+// Per block of 16*TT tokens a wave
+//   1. maps its tokens to slots through the block table (one page-id load per lane,
+//      fetched a block ahead and spread with ds_bpermute),
+//   2. loads K rows coalesced (whole rows per instruction) and stages them in a
+//      private padded LDS tile, from which it reads the MFMA A operand (lane l:
+//      token l%16, 16 bytes at 64*u + 16*(l/16) of the row),
+//   3. loads V rows coalesced straight into registers: the lane keeps 16-byte groups
+//      (256 bytes apart) of its 4*TT score-slot tokens,
 //   4. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp8 K is widened to
-//      bf16 exactly in registers), so each lane ends up with 8 scores of ONE row,
-//   5. runs the online softmax in the exp2 domain (row max across the 4 lanes
-//      of a row by two xor-shuffles, running sum kept per lane),
-//   6. computes O^T += V^T P^T: the lane's own 8 probabilities are the B operand
-//      (no data movement), and V^T's A operand is an 8x8 transpose done inside
-//      the lane's registers (the column permutation is undone on the write).
-// The waves of a row group then merge through LDS in a fixed order (bitwise
-// deterministic) and the last one writes the split's partial O (normalised,
+//      bf16 exactly in registers), so each lane ends up with scores of ONE row,
+//   5. runs the online softmax in the exp2 domain (row max across the 4 lanes of a
+//      row by two xor-shuffles, running sum kept per lane),
+//   6. computes O^T += V^T P^T: the lane's own probabilities are the B operand (no
+//      data movement) and V^T's A operand is a transpose inside the lane's
+//      registers (the column permutation is undone when the partial is written).
+// For d = 128 the next block's K/V loads are in flight while a block computes.
+// The last wave of each (head, row group) writes the split's partial O (normalised,
 // times v_scale) and LSE (natural log) to the workspace.
 //
 // Masking: the tail of a split and, with a left window W, keys t < L + i - W of
@@ -72,60 +77,240 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t x) {
   return r;
 }
 
-template <int NB>
-__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* dst) {
-  if constexpr (NB == 8) {
-    u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    dst[0] = v[0];
-    dst[1] = v[1];
-  } else {
+// Block geometry for one KV head: K rows of qk_dim elements, V rows of v_dim.
+template <int DK, int DV, bool FP8, int TT>
+struct Geo {
+  static constexpr int EB = FP8 ? 1 : 2;
+  static constexpr int TB = 16 * TT;            // tokens per block
+  static constexpr int KRB = DK * EB;           // K row bytes
+  static constexpr int KCH = KRB / 16;          // 16-byte chunks per K row
+  static constexpr int NKLD = TB * KCH / 64;    // coalesced K loads per lane per block
+  static constexpr int RS = KRB + 16;           // LDS row stride; +16 keeps reads conflict-free
+  static constexpr int TILE = TB * RS;          // LDS bytes of one wave's K tile
+  static constexpr int KU = KRB / 64;           // 16-byte operand chunks per lane per token
+  static constexpr int KSTEPS = DK / 32;        // MFMA k-steps
+  static constexpr int VRB = DV * EB;           // V row bytes read
+  static constexpr int VG = VRB >= 256 ? VRB / 256 : 1;   // V groups per lane per token
+  static constexpr int VGB = VRB >= 256 ? 16 : VRB / 16;  // bytes per group
+  static constexpr int VW = VG * VGB / 4;       // V dwords per lane per token
+  static constexpr int EPG = VGB / EB;          // V elements per group
+  static constexpr int CG = 256 / EB;           // elements spanned by one 256-byte group stride
+  static constexpr int CPL = DV / 16;           // O^T column tiles = V columns per lane
+  static_assert((TB * KCH) % 64 == 0, "whole K loads per block");
+  static_assert(CPL == VG * EPG, "V groups cover the lane's columns");
+  static_assert(KRB % 64 == 0, "K operand chunks");
+};
+
+template <class G>
+struct KVRegs {
+  u32x4 k[G::NKLD];               // coalesced K chunks, staged to LDS
+  uint32_t v[4 * G::TB / 16][G::VW];  // V groups of the lane's score-slot tokens
+};
+
+// Slot of token t0 + (lane % tb), clamped to the split's last token: one page-id
+// load per lane covers a whole block; other lanes read it with ds_bpermute.
+__device__ __forceinline__ int lane_slot(const int32_t* bt_row, int t0, int t_last, int lane,
+                                         int tb, int lg, int pmask) {
+  const int t = min(t0 + (lane & (tb - 1)), t_last);
+  return (bt_row[t >> lg] << lg) | (t & pmask);
+}
+
+// Token of S^T slot i (0 .. 4*TT-1) of lane group j: the 16x16 accumulator of token
+// tile tt holds tokens 16*tt + 4*j + r (r = 0..3) in a lane.  P^T and V^T use the
+// same slot order, which is all the MFMA reduction needs.
+__device__ __forceinline__ int slot_token(int j, int i) { return 16 * (i >> 2) + 4 * j + (i & 3); }
+
+template <class G>
+__device__ __forceinline__ void load_block(KVRegs<G>& R, int lslot, const uint8_t* kg,
+                                           const uint8_t* vg, int64_t k_sslot, int64_t v_sslot,
+                                           int lane, int n, int j) {
 #pragma unroll
-    for (int c = 0; c < NB / 16; ++c) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * c);
-      dst[4 * c + 0] = v[0];
-      dst[4 * c + 1] = v[1];
-      dst[4 * c + 2] = v[2];
-      dst[4 * c + 3] = v[3];
+  for (int u = 0; u < G::NKLD; ++u) {
+    const int q = 64 * u + lane;
+    const int sl = __shfl(lslot, q / G::KCH, 64);
+    R.k[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)sl * k_sslot + 16 * (q % G::KCH));
+  }
+#pragma unroll
+  for (int i = 0; i < 4 * G::TB / 16; ++i) {
+    const int sl = __shfl(lslot, slot_token(j, i), 64);
+    const uint8_t* vp = vg + (int64_t)sl * v_sslot + G::VGB * n;
+#pragma unroll
+    for (int c = 0; c < G::VG; ++c) {
+      if constexpr (G::VGB == 16) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vp + 256 * c);
+        R.v[i][4 * c + 0] = x[0];
+        R.v[i][4 * c + 1] = x[1];
+        R.v[i][4 * c + 2] = x[2];
+        R.v[i][4 * c + 3] = x[3];
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+        R.v[i][0] = x[0];
+        R.v[i][1] = x[1];
+      }
     }
   }
 }
 
-// Token position of slot i (0..7) of lane group j inside a 32-token block.  The
-// S^T accumulator of token tile tt holds tokens 16*tt + 4*j + r (r = 0..3) in a
-// lane, so slots 0..3 are tile 0 and slots 4..7 tile 1.  P^T and V^T use the same
-// order, which is all the MFMA reduction needs.
-__device__ __forceinline__ int slot_token(int j, int i) {
-  return (i < 4) ? (4 * j + i) : (16 + 4 * j + (i - 4));
+// K chunks -> the wave's LDS tile (row-major, stride RS).
+template <class G>
+__device__ __forceinline__ void stage_k(const KVRegs<G>& R, uint8_t* tile, int lane) {
+#pragma unroll
+  for (int u = 0; u < G::NKLD; ++u) {
+    const int q = 64 * u + lane;
+    *reinterpret_cast<u32x4*>(tile + (q / G::KCH) * G::RS + 16 * (q % G::KCH)) = R.k[u];
+  }
 }
 
-__device__ __forceinline__ int64_t token_slot(const int32_t* bt_row, int t, int lg, int pmask) {
-  const int page = bt_row[t >> lg];
-  return ((int64_t)page << lg) | (int64_t)(t & pmask);
+// Per-wave running state of the online softmax for RT row tiles.
+template <int DV, int RT>
+struct RowState {
+  float m[RT], l[RT];
+  f32x4 o[RT][DV / 16];
+};
+
+template <class G, bool FP8, int RT, int DV>
+__device__ __forceinline__ void compute_block(const uint8_t* tile, const KVRegs<G>& R,
+                                              const bf16x8 (&qB)[RT][G::KSTEPS],
+                                              const int (&row_lo)[RT], RowState<DV, RT>& st,
+                                              int t0, int t_end, float c_log2, int n, int j) {
+  constexpr int TT = G::TB / 16;
+  constexpr int NS = 4 * TT;  // scores per lane per row tile
+  constexpr int CPL = G::CPL;
+
+  // a4: S^T = K Q^T, K operand chunks read from the LDS tile
+  f32x4 sacc[TT][RT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sacc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ku = 0; ku < G::KU; ++ku) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const u32x4 c =
+          *reinterpret_cast<const u32x4*>(tile + (16 * tt + n) * G::RS + 64 * ku + 16 * j);
+      if constexpr (FP8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x2 w0 = fp8x4_to_bf16x4(c[2 * h]);
+          const u32x2 w1 = fp8x4_to_bf16x4(c[2 * h + 1]);
+          const bf16x8 a = as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            sacc[tt][rt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[rt][2 * ku + h], sacc[tt][rt], 0, 0, 0);
+        }
+      } else {
+        const bf16x8 a = as_bf16x8(c);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          sacc[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[rt][ku], sacc[tt][rt], 0, 0, 0);
+      }
+    }
+  }
+
+  // online softmax in the exp2 domain; the lane holds NS scores of one row per tile
+  uint32_t pbits[RT][NS / 2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float sc[NS];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+      const int t = t0 + 16 * (e >> 2) + 4 * j + (e & 3);
+      const bool ok = (t < t_end) && (t >= row_lo[rt]);
+      const float v = ok ? sacc[e >> 2][rt][e & 3] * c_log2 : -INFINITY;
+      sc[e] = v;
+      bmax = fmaxf(bmax, v);
+    }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const float m_new = fmaxf(st.m[rt], bmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m[rt] - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+      sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+      psum += sc[e];
+    }
+    st.l[rt] = st.l[rt] * alpha + psum;
+    st.m[rt] = m_new;
+#pragma unroll
+    for (int ct = 0; ct < CPL; ++ct) st.o[rt][ct] *= alpha;
+#pragma unroll
+    for (int e = 0; e < NS; e += 2) {
+      const __bf16 lo = (__bf16)sc[e], hi = (__bf16)sc[e + 1];
+      pbits[rt][e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+  }
+
+  // a5: O^T += V^T P^T.  Column tile ct = (group c, element e) holds, in row m,
+  // column c*CG + EPG*m + e.
+#pragma unroll
+  for (int ct = 0; ct < CPL; ++ct) {
+    const int c = ct / G::EPG, e = ct % G::EPG;
+    uint32_t av[NS / 2];
+    if constexpr (FP8) {
+      const int w = c * (G::VGB / 4) + e / 4, sh = 8 * (e & 3);
+#pragma unroll
+      for (int h = 0; h < NS / 4; ++h) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x |= ((R.v[4 * h + k][w] >> sh) & 0xffu) << (8 * k);
+        const u32x2 cv = fp8x4_to_bf16x4(x);
+        av[2 * h] = cv[0];
+        av[2 * h + 1] = cv[1];
+      }
+    } else {
+      const int w = c * (G::VGB / 4) + e / 2;
+#pragma unroll
+      for (int q2 = 0; q2 < NS / 2; ++q2) {
+        const uint32_t a0 = R.v[2 * q2][w], a1 = R.v[2 * q2 + 1][w];
+        av[q2] = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (TT == 2) {
+        st.o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(u32x4{av[0], av[1], av[2], av[3]}),
+            as_bf16x8(u32x4{pbits[rt][0], pbits[rt][1], pbits[rt][2], pbits[rt][3]}),
+            st.o[rt][ct], 0, 0, 0);
+      } else {
+        st.o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(s16x4, u32x2{av[0], av[1]}),
+            __builtin_bit_cast(s16x4, u32x2{pbits[rt][0], pbits[rt][1]}), st.o[rt][ct], 0, 0, 0);
+      }
+    }
+  }
 }
 
 }  // namespace
 
-template <int DK, int DV, bool FP8, int RT, int NRG>
-__global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int KSTEPS = DK / 32;          // MFMA k-steps over qk_dim
-  constexpr int KLOADS = DK * EB / 64;     // 16-B K loads per lane per token tile
-  constexpr int CPL = DV / 16;             // V columns per lane per token (= O^T col tiles)
-  constexpr int VBYTES = CPL * EB;
-  constexpr int VW = VBYTES / 4;
-  constexpr int NTL = kWaves / NRG;        // waves sharing one row group
-  static_assert(DK % 64 == 0 || !FP8, "fp8 K loads cover two k-steps");
-  static_assert(VBYTES == 8 || VBYTES % 16 == 0, "V chunk");
+template <int DK, int DV, bool FP8, int RT, int NRG, int NTL, int TT, bool PIPE, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
+void splitkv_fwd_kernel(FwdParams P) {
+  using G = Geo<DK, DV, FP8, TT>;
+  constexpr int KSTEPS = G::KSTEPS;
+  constexpr int CPL = G::CPL;
+  constexpr int HPC = kWaves / (NRG * NTL);
+  constexpr int TB = G::TB;
+  static_assert(HPC * NRG * NTL == kWaves, "wave layout");
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[kWaves][G::TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int j = lane >> 4;
-  const int rg = wave % NRG;
-  const int tl = wave / NRG;
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
+  const int hc = wave / (NRG * NTL);
+  const int rg = (wave / NTL) % NRG;
+  const int tl = wave % NTL;
+  const int g = blockIdx.x * HPC + hc;     // KV head of this wave
+  const int s = blockIdx.y;
   const int b = blockIdx.z;
+  const bool head_ok = g < P.hkv;          // the last head group may be partial
 
   // a2: this split's slice of the attended prefix [lo, L)
   const int L = P.prefix_lens[b];
@@ -134,7 +319,7 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
   if (s >= nsplit) return;  // uniform over the workgroup, before any barrier
   const int t_begin = lo + s * P.chunk;
   const int t_end = (s == P.splits - 1) ? L : min(L, t_begin + P.chunk);
-  const int nblk = (t_end - t_begin + kTokBlock - 1) / kTokBlock;
+  const int nblk = head_ok ? (t_end - t_begin + TB - 1) / TB : 0;
 
   // Q^T as the B operand: lane holds row n of each row tile, 8 consecutive k-slots.
   bf16x8 qB[RT][KSTEPS];
@@ -142,7 +327,7 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = (rg * RT + rt) * 16 + n;
-    const bool rv = row < P.rows;
+    const bool rv = head_ok && row < P.rows;
     const int i = rv ? row / P.group : 0;
     const int hh = rv ? row % P.group : 0;
     row_lo[rt] = P.window >= 0 ? L + i - P.window : INT_MIN;
@@ -150,7 +335,7 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
         P.q + (int64_t)(b * P.draft + i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      // element offset of this lane's 8 k-slots; must match the K operand below
+      // element offset of this lane's 8 k-slots; matches the K operand chunk layout
       const int d0 = FP8 ? (64 * (ks / 2) + 16 * j + 8 * (ks % 2)) : (32 * ks + 8 * j);
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (rv) raw = *reinterpret_cast<const u32x4*>(qp + 2 * d0);
@@ -158,131 +343,65 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
     }
   }
 
-  float m_run[RT], l_run[RT];
-  f32x4 oacc[RT][CPL];
+  RowState<DV, RT> st;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+    st.m[rt] = -INFINITY;
+    st.l[rt] = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < CPL; ++ct) oacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CPL; ++ct) st.o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-  const uint8_t* kbase = P.k + (int64_t)g * P.k_shead + 16 * j;
-  const uint8_t* vbase = P.v + (int64_t)g * P.v_shead + n * VBYTES;
+  const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
+  const uint8_t* vg = P.v + (int64_t)g * P.v_shead;
+  uint8_t* tile = s_tile[wave];
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
+  const int t_last = t_end - 1;
+  auto t0_of = [&](int bk) { return t_begin + bk * TB; };
 
-  for (int blk = tl; blk < nblk; blk += NTL) {
-    const int t0 = t_begin + blk * kTokBlock;
-
-    // a3: gather.  K: token 16*tt + n of the block.  V: the lane's 8 slot tokens.
-    u32x4 kraw[2][KLOADS];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = min(t0 + 16 * tt + n, t_end - 1);
-      const uint8_t* kp = kbase + token_slot(bt_row, t, lg, pmask) * P.k_sslot;
-#pragma unroll
-      for (int u = 0; u < KLOADS; ++u) kraw[tt][u] = *reinterpret_cast<const u32x4*>(kp + 64 * u);
-    }
-    uint32_t vraw[8][VW];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = min(t0 + slot_token(j, e), t_end - 1);
-      load_bytes<VBYTES>(vbase + token_slot(bt_row, t, lg, pmask) * P.v_sslot, vraw[e]);
-    }
-
-    // a4: S^T = K Q^T
-    f32x4 sacc[2][RT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) sacc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        bf16x8 a;
-        if constexpr (FP8) {
-          const u32x4 c = kraw[tt][ks / 2];
-          const u32x2 w0 = fp8x4_to_bf16x4(c[2 * (ks % 2)]);
-          const u32x2 w1 = fp8x4_to_bf16x4(c[2 * (ks % 2) + 1]);
-          a = as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]});
-        } else {
-          a = as_bf16x8(kraw[tt][ks]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          sacc[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[rt][ks], sacc[tt][rt], 0, 0, 0);
+  // a3: this wave's blocks are tl, tl+NTL, ...
+  int blk = tl;
+  if (blk < nblk) {
+    if constexpr (PIPE) {
+      // next block's K/V loads in flight while a block computes (register sets A/B)
+      int sl_next = 0, sl_after = 0;
+      const int sl0 = lane_slot(bt_row, t0_of(blk), t_last, lane, TB, lg, pmask);
+      if (blk + NTL < nblk) sl_next = lane_slot(bt_row, t0_of(blk + NTL), t_last, lane, TB, lg, pmask);
+      KVRegs<G> A, Bk;
+      load_block<G>(A, sl0, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
+      stage_k<G>(A, tile, lane);
+      for (;;) {
+        const int b1 = blk + NTL, b2 = blk + 2 * NTL;
+        if (b1 < nblk) load_block<G>(Bk, sl_next, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
+        if (b2 < nblk) sl_after = lane_slot(bt_row, t0_of(b2), t_last, lane, TB, lg, pmask);
+        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, st, t0_of(blk), t_end, P.c_log2, n, j);
+        if (b1 >= nblk) break;
+        stage_k<G>(Bk, tile, lane);
+        const int b3 = blk + 3 * NTL;
+        if (b2 < nblk) load_block<G>(A, sl_after, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
+        if (b3 < nblk) sl_next = lane_slot(bt_row, t0_of(b3), t_last, lane, TB, lg, pmask);
+        compute_block<G, FP8, RT, DV>(tile, Bk, qB, row_lo, st, t0_of(b1), t_end, P.c_log2, n, j);
+        if (b2 >= nblk) break;
+        stage_k<G>(A, tile, lane);
+        blk = b2;
       }
-    }
-
-    // online softmax (exp2 domain); lane holds 8 scores of row n of each row tile
-    bf16x8 pB[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float sc[8];
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tt = e >> 2, r = e & 3;
-        const int t = t0 + 16 * tt + 4 * j + r;
-        const bool ok = (t < t_end) && (t >= row_lo[rt]);
-        const float v = ok ? sacc[tt][rt][r] * P.c_log2 : -INFINITY;
-        sc[e] = v;
-        bmax = fmaxf(bmax, v);
+    } else {
+      int sl = lane_slot(bt_row, t0_of(blk), t_last, lane, TB, lg, pmask);
+      for (; blk < nblk; blk += NTL) {
+        KVRegs<G> A;
+        load_block<G>(A, sl, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
+        if (blk + NTL < nblk) sl = lane_slot(bt_row, t0_of(blk + NTL), t_last, lane, TB, lg, pmask);
+        stage_k<G>(A, tile, lane);
+        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, st, t0_of(blk), t_end, P.c_log2, n, j);
       }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float m_new = fmaxf(m_run[rt], bmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
-        psum += sc[e];
-      }
-      l_run[rt] = l_run[rt] * alpha + psum;
-      m_run[rt] = m_new;
-#pragma unroll
-      for (int ct = 0; ct < CPL; ++ct) oacc[rt][ct] *= alpha;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[e];
-      pB[rt] = pb;
-    }
-
-    // a5: O^T += V^T P^T.  Column tile ct holds column CPL*m + ct in row m.
-#pragma unroll
-    for (int ct = 0; ct < CPL; ++ct) {
-      u32x4 av;
-      if constexpr (FP8) {
-        const int w = ct >> 2, sh = 8 * (ct & 3);
-        uint32_t x0 = 0, x1 = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x0 |= ((vraw[e][w] >> sh) & 0xffu) << (8 * e);
-          x1 |= ((vraw[4 + e][w] >> sh) & 0xffu) << (8 * e);
-        }
-        const u32x2 c0 = fp8x4_to_bf16x4(x0);
-        const u32x2 c1 = fp8x4_to_bf16x4(x1);
-        av = u32x4{c0[0], c0[1], c1[0], c1[1]};
-      } else {
-        const int w = ct >> 1;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const uint32_t a0 = vraw[2 * q2][w], a1 = vraw[2 * q2 + 1][w];
-          av[q2] = (ct & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        }
-      }
-      const bf16x8 a = as_bf16x8(av);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        oacc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pB[rt], oacc[rt][ct], 0, 0, 0);
     }
   }
+
+  float (&m_run)[RT] = st.m;
+  float (&l_run)[RT] = st.l;
+  f32x4 (&oacc)[RT][CPL] = st.o;
 
   // each lane summed only its own tokens: total the 4 lanes of a row
 #pragma unroll
@@ -292,10 +411,12 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
   }
 
   if constexpr (NTL > 1) {
-    // merge the waves of each row group in a fixed order through LDS
+    // merge the token lanes of each (head, row group) in a fixed order through LDS
     constexpr int NREG = RT * CPL * 4 + RT;
+    constexpr int NGRP = HPC * NRG;
+    const int grp = hc * NRG + rg;
     __shared__ float sm_m[kWaves][RT][16];
-    __shared__ float sm_o[NRG][NREG][64];
+    __shared__ float sm_o[NGRP][NREG][64];
     if (j == 0) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) sm_m[wave][rt][n] = m_run[rt];
@@ -305,7 +426,7 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
     for (int rt = 0; rt < RT; ++rt) {
       float M = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < NTL; ++k) M = fmaxf(M, sm_m[k * NRG + rg][rt][n]);
+      for (int k = 0; k < NTL; ++k) M = fmaxf(M, sm_m[grp * NTL + k][rt][n]);
       const float f = (m_run[rt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[rt] - M);
       l_run[rt] *= f;
 #pragma unroll
@@ -321,8 +442,8 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
 #pragma unroll
             for (int ct = 0; ct < CPL; ++ct)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) oacc[rt][ct][r] += sm_o[rg][(rt * CPL + ct) * 4 + r][lane];
-            l_run[rt] += sm_o[rg][RT * CPL * 4 + rt][lane];
+              for (int r = 0; r < 4; ++r) oacc[rt][ct][r] += sm_o[grp][(rt * CPL + ct) * 4 + r][lane];
+            l_run[rt] += sm_o[grp][RT * CPL * 4 + rt][lane];
           }
         }
         if (k < NTL - 1) {
@@ -331,8 +452,8 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
 #pragma unroll
             for (int ct = 0; ct < CPL; ++ct)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) sm_o[rg][(rt * CPL + ct) * 4 + r][lane] = oacc[rt][ct][r];
-            sm_o[rg][RT * CPL * 4 + rt][lane] = l_run[rt];
+              for (int r = 0; r < 4; ++r) sm_o[grp][(rt * CPL + ct) * 4 + r][lane] = oacc[rt][ct][r];
+            sm_o[grp][RT * CPL * 4 + rt][lane] = l_run[rt];
           }
         }
       }
@@ -340,8 +461,10 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
     }
     if (tl != NTL - 1) return;
   }
+  if (!head_ok) return;
 
-  // write the split's partial: lane holds row n, columns [4*CPL*j, 4*CPL*(j+1))
+  // write the split's partial.  Lane holds row n; for group c and r = 0..3 the
+  // columns c*CG + EPG*(4*j + r) + [0, EPG).
   const int64_t split_id = ((int64_t)b * P.hkv + g) * P.splits + s;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -349,15 +472,18 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
     if (row >= P.rows) continue;
     const float l = l_run[rt];
     const float inv = l > 0.f ? P.v_scale / l : 0.f;
-    float* po = P.part_o + (split_id * P.rows + row) * DV + 4 * CPL * j;
+    float* po = P.part_o + (split_id * P.rows + row) * DV;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int c = 0; c < G::VG; ++c) {
 #pragma unroll
-      for (int c4 = 0; c4 < CPL; c4 += 4) {
-        f32x4 o;
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = oacc[rt][c4 + c][r] * inv;
-        *reinterpret_cast<f32x4*>(po + CPL * r + c4) = o;
+        for (int e4 = 0; e4 < G::EPG; e4 += 4) {
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = oacc[rt][c * G::EPG + e4 + e][r] * inv;
+          *reinterpret_cast<f32x4*>(po + c * G::CG + G::EPG * (4 * j + r) + e4) = o;
+        }
       }
     }
     if (j == 0)
@@ -367,25 +493,46 @@ __global__ __launch_bounds__(256) void splitkv_fwd_kernel(FwdParams P) {
 
 namespace {
 
+// Kernel variant per wave layout.  d = 128: 32-token blocks, K/V double-buffered.
+// d = 256: 32-token blocks, single buffer (a second one would not fit beside the
+// 32x256 accumulator).  d = 576/512: 16-token blocks, single buffer.
 template <int DK, int DV, bool FP8>
 int launch_dims(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {
-#define VA_LAUNCH(RT_, NRG_) \
-  hipLaunchKernelGGL((splitkv_fwd_kernel<DK, DV, FP8, RT_, NRG_>), grid, dim3(256), 0, st, fp)
+  constexpr int TT = DK >= 576 ? 1 : 2;
+  constexpr bool PIPE = DK == 128;
+  // with one 16-row tile the double-buffered d = 128 kernel fits two waves per SIMD
+#define VA_LAUNCH(RT_, NRG_, NTL_)                                                              \
+  return launch_kernel(reinterpret_cast<const void*>(                                           \
+                           &splitkv_fwd_kernel<DK, DV, FP8, RT_, NRG_, NTL_, TT, PIPE,          \
+                                               (DK == 128 && RT_ == 1) ? 2 : 1>),               \
+                       grid, dim3(256), fp, st)
+  const int key = p.rt * 100 + p.nrg * 10 + p.ntl;
   if constexpr (DV > 256) {
     // a 512-wide O^T already fills 128 accumulator registers: one row tile per wave
-    if (p.rt == 1 && p.nrg == 1) VA_LAUNCH(1, 1);
-    else if (p.rt == 1 && p.nrg == 2) VA_LAUNCH(1, 2);
-    else if (p.rt == 1 && p.nrg == 4) VA_LAUNCH(1, 4);
-    else return VA_EUNSUPPORTED;
+    switch (key) {
+      case 111: VA_LAUNCH(1, 1, 1);
+      case 112: VA_LAUNCH(1, 1, 2);
+      case 114: VA_LAUNCH(1, 1, 4);
+      case 121: VA_LAUNCH(1, 2, 1);
+      case 122: VA_LAUNCH(1, 2, 2);
+      case 141: VA_LAUNCH(1, 4, 1);
+      default: return VA_EUNSUPPORTED;
+    }
   } else {
-    if (p.rt == 1 && p.nrg == 1) VA_LAUNCH(1, 1);
-    else if (p.rt == 2 && p.nrg == 1) VA_LAUNCH(2, 1);
-    else if (p.rt == 2 && p.nrg == 2) VA_LAUNCH(2, 2);
-    else if (p.rt == 2 && p.nrg == 4) VA_LAUNCH(2, 4);
-    else return VA_EUNSUPPORTED;
+    switch (key) {
+      case 111: VA_LAUNCH(1, 1, 1);
+      case 112: VA_LAUNCH(1, 1, 2);
+      case 114: VA_LAUNCH(1, 1, 4);
+      case 211: VA_LAUNCH(2, 1, 1);
+      case 212: VA_LAUNCH(2, 1, 2);
+      case 214: VA_LAUNCH(2, 1, 4);
+      case 221: VA_LAUNCH(2, 2, 1);
+      case 222: VA_LAUNCH(2, 2, 2);
+      case 241: VA_LAUNCH(2, 4, 1);
+      default: return VA_EUNSUPPORTED;
+    }
   }
 #undef VA_LAUNCH
-  return hipGetLastError() == hipSuccess ? VA_OK : VA_EHIP;
 }
 
 }  // namespace
@@ -418,7 +565,7 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.chunk = p.chunk;
   fp.c_log2 = a->sm_scale * a->k_scale * kLog2e;
   fp.v_scale = a->v_scale;
-  const dim3 grid(p.splits, a->hkv, a->batch);
+  const dim3 grid((a->hkv + p.hpc - 1) / p.hpc, p.splits, a->batch);
   const bool f8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
   if (a->qk_dim == 128) return f8 ? launch_dims<128, 128, true>(fp, p, grid, st)
                                   : launch_dims<128, 128, false>(fp, p, grid, st);

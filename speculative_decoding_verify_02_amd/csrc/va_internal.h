@@ -13,6 +13,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;  // 16x16x16 MFMA operand
 
 constexpr int kTokBlock = 32;   // prefix tokens one wave handles per main-loop step
 constexpr int kWaves = 4;       // waves per split-KV workgroup
@@ -23,7 +24,9 @@ struct Plan {
   int rows;         // G * D query rows per KV head
   int group;        // G
   int rt;           // 16-row MFMA tiles per wave (1 or 2)
-  int nrg;          // row groups per workgroup (1, 2, 4); waves per row group = 4 / nrg
+  int nrg;          // row groups of one KV head (1, 2, 4)
+  int ntl;          // token lanes: waves that interleave one (head, row group)'s blocks
+  int hpc;          // KV heads per workgroup; hpc * nrg * ntl = 4 waves
   int lg_page;      // log2(page_size)
   int splits;       // split slots per (sequence, KV head)
   int chunk;        // prefix tokens per split (multiple of kTokBlock)
@@ -43,5 +46,15 @@ int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t stream)
 
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();
+
+// Launches a kernel taking one by-value parameter struct.  The status comes from this
+// launch alone (not from the runtime's sticky last-error slot, which other code in
+// the process may have left set).
+template <typename Params>
+inline int launch_kernel(const void* fn, dim3 grid, dim3 block, const Params& params,
+                         hipStream_t stream) {
+  void* args[] = {const_cast<Params*>(&params)};
+  return hipLaunchKernel(fn, grid, block, args, 0, stream) == hipSuccess ? VA_OK : VA_EHIP;
+}
 
 }  // namespace va

@@ -116,6 +116,11 @@ int make_plan(const verify_attn_args* a, Plan* p) {
   const int groups = (tiles + p->rt - 1) / p->rt;
   p->nrg = groups <= 1 ? 1 : (groups <= 2 ? 2 : (groups <= 4 ? 4 : 0));
   if (p->nrg == 0) return VA_EUNSUPPORTED;
+  // the remaining waves of a workgroup cover more KV heads of the same tokens, then
+  // interleave tokens of one head
+  const int free_waves = kWaves / p->nrg;
+  p->hpc = a->hkv >= free_waves ? free_waves : (a->hkv >= 2 && free_waves >= 2 ? 2 : 1);
+  p->ntl = free_waves / p->hpc;
   p->lg_page = ilog2(a->page_size);
   p->max_leff = max_attended_prefix(a->max_prefix_len, a->window_left);
   p->splits = a->num_splits > 0

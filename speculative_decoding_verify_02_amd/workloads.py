@@ -157,14 +157,16 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
                  v_aliases_k: bool = False, sm_scale: Optional[float] = None,
                  window_left: int = -1, num_splits: int = 0,
                  num_pages: Optional[int] = None, pool_factor: float = 1.25,
-                 seed: int = 0, poison: bool = False) -> Problem:
+                 seed: int = 0, poison: bool = False, shuffle_pages: bool = True) -> Problem:
     """Draw one problem.
 
     ``prefix_lens``: explicit list, or ``prefix_range=(lo, hi)`` for
     uniform integers in [lo, hi].  ``num_pages`` fixes the pool size, else
     ``ceil(pool_factor * total pages)``.  With ``poison`` the pool's page 0 is
     reserved and every slot no sequence owns (including the unused tail of a
-    sequence's last page) holds NaN bit patterns.
+    sequence's last page) holds NaN bit patterns.  ``shuffle_pages=False`` hands
+    out pages in pool order (each sequence's pages contiguous), the layout a
+    fresh allocator would produce.
     """
     v_dim = qk_dim if v_dim is None else v_dim
     if sm_scale is None:
@@ -189,7 +191,10 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
         num_pages = max(int(math.ceil(pool_factor * total_pages)), total_pages) + reserved
     if num_pages - reserved < total_pages:
         raise ValueError("pool too small")
-    perm = rng.permutation(num_pages - reserved)[:total_pages] + reserved
+    if shuffle_pages:
+        perm = rng.permutation(num_pages - reserved)[:total_pages] + reserved
+    else:
+        perm = np.arange(total_pages) + reserved
     page_ids = []
     indptr = np.zeros(batch + 1, dtype=np.int64)
     indices = np.empty(int(n_tok.sum()), dtype=np.int64)
