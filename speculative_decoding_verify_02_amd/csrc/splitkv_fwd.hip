@@ -42,22 +42,6 @@
 
 namespace va {
 
-struct FwdParams {
-  const uint8_t* q;  // bf16
-  int64_t q_srow, q_shead;   // bytes
-  const uint8_t* k;
-  int64_t k_sslot, k_shead;  // bytes
-  const uint8_t* v;
-  int64_t v_sslot, v_shead;  // bytes
-  const int32_t* bt;
-  int32_t max_pages;
-  const int32_t* prefix_lens;
-  float* part_o;
-  float* part_lse;
-  int hkv, group, draft, rows, lg_page, window, splits, chunk;
-  float c_log2;  // sm_scale * k_scale * log2(e)
-  float v_scale;
-};
 
 namespace {
 
@@ -538,6 +522,7 @@ int launch_dims(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {
 }  // namespace
 
 int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st) {
+  const bool mla_fp8 = a->kv_dtype == VA_KV_FP8_E4M3FN && a->qk_dim == 576 && p.rows <= 64;
   if (a->batch > 65535 || a->hkv > 65535) return VA_EUNSUPPORTED;
   const int eb = a->kv_dtype == VA_KV_FP8_E4M3FN ? 1 : 2;
   FwdParams fp;
@@ -565,6 +550,7 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.chunk = p.chunk;
   fp.c_log2 = a->sm_scale * a->k_scale * kLog2e;
   fp.v_scale = a->v_scale;
+  if (mla_fp8) return launch_splitkv_mla_fp8(fp, p, dim3(a->hkv, p.splits, a->batch), st);
   const dim3 grid((a->hkv + p.hpc - 1) / p.hpc, p.splits, a->batch);
   const bool f8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
   if (a->qk_dim == 128) return f8 ? launch_dims<128, 128, true>(fp, p, grid, st)

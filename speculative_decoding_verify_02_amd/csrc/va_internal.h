@@ -34,6 +34,24 @@ struct Plan {
   int64_t ws_o_floats;  // offset of partial LSEs in the workspace (floats)
 };
 
+// Split-KV kernel parameters (strides in bytes), resolved from verify_attn_args.
+struct FwdParams {
+  const uint8_t* q;  // bf16
+  int64_t q_srow, q_shead;   // bytes
+  const uint8_t* k;
+  int64_t k_sslot, k_shead;  // bytes
+  const uint8_t* v;
+  int64_t v_sslot, v_shead;  // bytes
+  const int32_t* bt;
+  int32_t max_pages;
+  const int32_t* prefix_lens;
+  float* part_o;
+  float* part_lse;
+  int hkv, group, draft, rows, lg_page, window, splits, chunk;
+  float c_log2;  // sm_scale * k_scale * log2(e)
+  float v_scale;
+};
+
 // Validates args (host only) and fills the plan.  Returns a VA_ status.
 int make_plan(const verify_attn_args* a, Plan* plan);
 
@@ -42,6 +60,8 @@ int launch_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int3
                        int lg_page, int32_t max_pages, int32_t* block_table, int32_t* kv_lens,
                        hipStream_t stream);
 int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t stream);
+// fp8 MLA heads (qk_dim 576, v_dim 512 = first 512 of the K row), <= 64 rows per head.
+int launch_splitkv_mla_fp8(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t stream);
 int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t stream);
 
 // Compute-unit count of the current device (cached per device).
