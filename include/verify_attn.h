@@ -162,12 +162,13 @@ int verify_attn_combine(const verify_attn_args* args, void* stream);
 int verify_attn_can_handle(const verify_attn_args* args);
 
 /*
- * Split slots per (sequence, KV head) that the heuristic picks for this shape on
- * the current device (from its compute-unit count).  Host only.  Returns >= 1, or
- * -1 on invalid input.
+ * Split slots per (sequence, KV head) that the heuristic picks for these arguments
+ * on the current device (from its compute-unit count and the kernel the arguments
+ * select); args->num_splits is ignored.  Host only, reads no device memory: the
+ * pointers may still be unset.  Returns >= 1, or -1 when the arguments are rejected
+ * (the status verify_attn_can_handle would give).
  */
-int32_t verify_attn_num_splits(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
-                               int32_t v_dim, int32_t max_prefix_len, int32_t window_left);
+int32_t verify_attn_num_splits(const verify_attn_args* args);
 
 /*
  * Workspace bytes needed for num_splits split slots (>= 1):

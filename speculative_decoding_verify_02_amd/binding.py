@@ -100,7 +100,7 @@ def load(path: Optional[str] = None):
         getattr(lib, name).restype = ctypes.c_int
     lib.verify_attn_can_handle.argtypes = [args_p]
     lib.verify_attn_can_handle.restype = ctypes.c_int
-    lib.verify_attn_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.verify_attn_num_splits.argtypes = [args_p]
     lib.verify_attn_num_splits.restype = i32
     lib.verify_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.verify_attn_workspace_bytes.restype = i64
@@ -183,7 +183,8 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
     [num_slots, Hkv, >= v_dim] (bf16, or uint8 holding e4m3fn codes) - v_cache may be
     k_cache itself (MLA alias, give v_dim); block_table [B, max_pages] int32;
     prefix_lens [B] int32; out [B*D, Hq, v_dim] bf16; workspace a float32 tensor of
-    at least workspace_bytes(); lse [B*D, Hq] float32 or None."""
+    at least workspace_bytes() (or None while sizing it: see set_workspace); lse
+    [B*D, Hq] float32 or None."""
     qk_dim = q.shape[-1] if qk_dim is None else qk_dim
     v_dim = out.shape[-1] if v_dim is None else v_dim
     a = VerifyAttnArgs()
@@ -212,7 +213,7 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
     a.max_pages_per_seq = block_table.shape[1]
     a.prefix_lens = _ptr(prefix_lens)
     a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.out = _ptr(out)
     a.o_stride_row, a.o_stride_head = out.stride(0), out.stride(1)
     a.lse = _ptr(lse)
@@ -238,9 +239,16 @@ def verify_attn_can_handle(call: VerifyCall) -> int:
     return load().verify_attn_can_handle(ctypes.byref(call.args))
 
 
-def verify_attn_num_splits(batch, hkv, hq, draft_len, v_dim, max_prefix_len, window_left) -> int:
-    return load().verify_attn_num_splits(batch, hkv, hq, draft_len, v_dim, max_prefix_len,
-                                         window_left)
+def verify_attn_num_splits(call: VerifyCall) -> int:
+    """The heuristic's split count for these arguments (host only; -1 if rejected)."""
+    return load().verify_attn_num_splits(ctypes.byref(call.args))
+
+
+def set_workspace(call: VerifyCall, workspace) -> None:
+    """Point an existing call at a (new) workspace tensor."""
+    call.args.workspace = _ptr(workspace)
+    call.args.workspace_bytes = workspace.numel() * workspace.element_size()
+    call.tensors["workspace"] = workspace
 
 
 def verify_attn_workspace_bytes(batch, hkv, hq, draft_len, v_dim, num_splits) -> int:

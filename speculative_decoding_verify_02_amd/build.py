@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libverify_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["verify_attn.hip", "block_table.hip", "splitkv_fwd.hip", "splitkv_mla_fp8.hip", "combine.hip"]
+SOURCES = ["verify_attn.hip", "block_table.hip", "splitkv_fwd.hip", "splitkv_mla_fp8.hip", "splitkv_tile.hip",
+           "combine.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -522,7 +522,6 @@ int launch_dims(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {
 }  // namespace
 
 int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st) {
-  const bool mla_fp8 = a->kv_dtype == VA_KV_FP8_E4M3FN && a->qk_dim == 576 && p.rows <= 64;
   if (a->batch > 65535 || a->hkv > 65535) return VA_EUNSUPPORTED;
   const int eb = a->kv_dtype == VA_KV_FP8_E4M3FN ? 1 : 2;
   FwdParams fp;
@@ -550,7 +549,9 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.chunk = p.chunk;
   fp.c_log2 = a->sm_scale * a->k_scale * kLog2e;
   fp.v_scale = a->v_scale;
-  if (mla_fp8) return launch_splitkv_mla_fp8(fp, p, dim3(a->hkv, p.splits, a->batch), st);
+  if (p.kind == kMlaFp8) return launch_splitkv_mla_fp8(fp, p, dim3(a->hkv, p.splits, a->batch), st);
+  if (p.kind == kTile)
+    return launch_splitkv_tile(fp, a->qk_dim, p.hpc, p.nrg, dim3(a->hkv / p.hpc, p.splits, a->batch), st);
   const dim3 grid((a->hkv + p.hpc - 1) / p.hpc, p.splits, a->batch);
   const bool f8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
   if (a->qk_dim == 128) return f8 ? launch_dims<128, 128, true>(fp, p, grid, st)

@@ -1,0 +1,263 @@
+// Split-KV pass for bf16 GQA heads (qk_dim = v_dim = 128 or 256) that reads the
+// paged cache as whole slot rows.
+//
+// In the [slot, H_kv, d] layout (the paged view of PR #23146) the K rows of all
+// KV heads of one token are adjacent, and a page of P tokens is P * H_kv * d
+// contiguous elements.  A workgroup therefore takes HPC KV heads of one
+// (sequence, split) and loads each 16-token block cooperatively: every load
+// instruction reads whole runs of a slot row (all HPC heads), so HBM sees long
+// contiguous reads instead of one head's 256-byte slices.  K and V blocks go to
+// double-buffered LDS tiles (the next block loads while this one computes);
+// each wave then reads only its own head's slice:
+//   QK: A operand = K rows from LDS (ds_read_b128), B = the wave's Q^T rows held
+//       in registers, v_mfma_f32_16x16x32_bf16 -> S^T (16 tokens x 16 rows);
+//   softmax: online, exp2 domain, row max across the 4 lanes of a row;
+//   PV: O^T += V^T P^T with v_mfma_f32_16x16x16_bf16; the V^T operand (4 tokens
+//       of one column per lane) comes from one ds_read_b64_tr_b16 per 16
+//       columns: in each 16-lane group, lanes 4k..4k+3 address token row k's 16
+//       columns and lane c receives column c of the 4 rows; the lane's own 4
+//       probabilities are the B operand.
+// Waves: HPC heads x NRG row groups (16 rows each).  No merge between waves: each
+// wave owns its (head, rows) for the whole split and writes its partial.
+
+#include <limits.h>
+#include <math.h>
+
+#include "va_internal.h"
+
+namespace va {
+
+namespace {
+
+constexpr int kTB = 16;  // tokens per block
+constexpr float kLn2 = 0.69314718055994530942f;
+
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+template <int D, int HPC, int NRG>
+struct TileGeo {
+  static constexpr int W = HPC * NRG;             // waves per workgroup
+  static constexpr int RB = D * 2;                // bytes of one head's row
+  static constexpr int RS = HPC * RB + 16;        // LDS row stride (pad: conflict-free reads)
+  static constexpr int TILE = kTB * RS;           // bytes of one K (or V) tile
+  static constexpr int CH = HPC * RB / 16;        // 16-byte chunks per token row slice
+  static constexpr int NLD = kTB * CH / (64 * W); // loads per thread per block (K; same for V)
+  static_assert((kTB * CH) % (64 * W) == 0, "whole loads per thread");
+};
+
+}  // namespace
+
+template <int D, int HPC, int NRG>
+__global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams P) {
+  using G = TileGeo<D, HPC, NRG>;
+  constexpr int KS = D / 32;   // QK k-steps
+  constexpr int CT = D / 16;   // O^T column tiles
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][G::TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[2][G::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int j = lane >> 4;
+  const int hc = wave / NRG;          // head within the workgroup
+  const int rg = wave % NRG;          // row group of that head
+  const int g0 = blockIdx.x * HPC;    // first KV head of the workgroup (HPC divides H_kv)
+  const int g = g0 + hc;
+  const int s = blockIdx.y;
+  const int b = blockIdx.z;
+
+  // a2: this split's slice of the attended prefix [lo, L)
+  const int L = P.prefix_lens[b];
+  const int lo = P.window >= 0 ? max(0, L - P.window) : 0;
+  const int nsplit = (L - lo + P.chunk - 1) / P.chunk;
+  if (s >= nsplit) return;  // uniform over the workgroup, before any barrier
+  const int t_begin = lo + s * P.chunk;
+  const int t_end = (s == P.splits - 1) ? L : min(L, t_begin + P.chunk);
+  const int nblk = (t_end - t_begin + kTB - 1) / kTB;
+  const int t_last = t_end - 1;
+
+  // Q^T operands of this wave's 16 rows: k-step ks holds elements 32ks + 8j + [0, 8)
+  const int row = rg * 16 + n;
+  const bool rv = row < P.rows;
+  bf16x8 qB[KS];
+  {
+    const int i = rv ? row / P.group : 0;
+    const int hh = rv ? row % P.group : 0;
+    const uint8_t* qp =
+        P.q + (int64_t)(b * P.draft + i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (rv) raw = *reinterpret_cast<const u32x4*>(qp + 2 * (32 * ks + 8 * j));
+      qB[ks] = as_bf16x8(raw);
+    }
+  }
+  const int row_lo = (P.window >= 0 && rv) ? L + row / P.group - P.window : INT_MIN;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
+  const int lg = P.lg_page;
+  const int pmask = (1 << lg) - 1;
+  // this thread's load chunks: q = 64*W*u + tid -> token q / CH, head (q % CH) / (RB/16)
+  auto lane_slot = [&](int t0) {
+    const int t = min(t0 + (lane & (kTB - 1)), t_last);
+    return (bt_row[t >> lg] << lg) | (t & pmask);
+  };
+  // one register set holds the next block while this one computes
+  u32x4 kr[G::NLD], vr[G::NLD];
+  auto load = [&](int sl_lane) {
+#pragma unroll
+    for (int u = 0; u < G::NLD; ++u) {
+      const int q = 64 * G::W * u + tid;
+      const int tok = q / G::CH, c = q % G::CH;
+      const int hd = c / (G::RB / 16), cc = c % (G::RB / 16);
+      const int64_t slot = __shfl(sl_lane, tok, 64);
+      kr[u] = *reinterpret_cast<const u32x4*>(P.k + slot * P.k_sslot + (int64_t)(g0 + hd) * P.k_shead + 16 * cc);
+      vr[u] = *reinterpret_cast<const u32x4*>(P.v + slot * P.v_sslot + (int64_t)(g0 + hd) * P.v_shead + 16 * cc);
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < G::NLD; ++u) {
+      const int q = 64 * G::W * u + tid;
+      const int off = (q / G::CH) * G::RS + 16 * (q % G::CH);
+      *reinterpret_cast<u32x4*>(&kt[buf][off]) = kr[u];
+      *reinterpret_cast<u32x4*>(&vt[buf][off]) = vr[u];
+    }
+  };
+
+  int sl_next = 0;
+  {
+    const int sl0 = lane_slot(t_begin);
+    if (nblk > 1) sl_next = lane_slot(t_begin + kTB);
+    load(sl0);
+    stage(0);
+  }
+  __syncthreads();
+
+  const int hoff = hc * G::RB;
+  // transposed-read address of this lane inside a V tile: token row 4j + n/4, 4
+  // columns starting at 4*(n%4) of each 16-column tile
+  const int vlane = (4 * j + (n >> 2)) * G::RS + hoff + 8 * (n & 3);
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    const int t0 = t_begin + blk * kTB;
+    if (blk + 1 < nblk) {
+      load(sl_next);  // next block in flight during this block's math
+      if (blk + 2 < nblk) sl_next = lane_slot(t0 + 2 * kTB);
+    }
+
+    // a4: S^T = K Q^T for the block's 16 tokens
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kp = &kt[buf][n * G::RS + hoff + 16 * j];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 64 * ks)), qB[ks], sacc, 0, 0, 0);
+
+    // online softmax: lane holds row n's scores for tokens 4j + r
+    float sc[4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 4 * j + r;
+      const bool ok = (t < t_end) && (t >= row_lo);
+      sc[r] = ok ? sacc[r] * P.c_log2 : -INFINITY;
+      bmax = fmaxf(bmax, sc[r]);
+    }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_use);
+      psum += sc[r];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) oacc[ct] *= alpha;
+    }
+    const __bf16 p0 = (__bf16)sc[0], p1 = (__bf16)sc[1], p2 = (__bf16)sc[2], p3 = (__bf16)sc[3];
+    const s16x4 pB = {__builtin_bit_cast(short, p0), __builtin_bit_cast(short, p1),
+                      __builtin_bit_cast(short, p2), __builtin_bit_cast(short, p3)};
+
+    // a5: O^T += V^T P^T, V^T from transposed LDS reads
+    __attribute__((address_space(3))) char* vb =
+        (__attribute__((address_space(3))) char*)vt[buf] + vlane;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(vb + 32 * ct));
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB, oacc[ct], 0, 0, 0);
+    }
+
+    if (blk + 1 < nblk) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // each lane summed only its own tokens: total the 4 lanes of the row
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!rv) return;
+  const int64_t split_id = ((int64_t)b * P.hkv + g) * P.splits + s;
+  const float inv = l_run > 0.f ? P.v_scale / l_run : 0.f;
+  // lane holds O[row][16ct + 4j + r], r = 0..3
+  float* po = P.part_o + (split_id * P.rows + row) * D + 4 * j;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    f32x4 o = oacc[ct];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] *= inv;
+    *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
+  }
+  if (j == 0)
+    P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+namespace {
+
+template <int D>
+int launch_d(const FwdParams& fp, int hpc, int nrg, dim3 grid, hipStream_t st) {
+#define VA_TILE(H_, R_)                                                                      \
+  return launch_kernel(reinterpret_cast<const void*>(&splitkv_tile_kernel<D, H_, R_>), grid, \
+                       dim3(64 * (H_) * (R_)), fp, st)
+  switch (hpc * 10 + nrg) {
+    case 11: VA_TILE(1, 1);
+    case 21: VA_TILE(2, 1);
+    case 41: VA_TILE(4, 1);
+    case 81:
+      if constexpr (D == 128) { VA_TILE(8, 1); }  // 8 heads x 256 B rows: 132 KB of LDS
+      return VA_EUNSUPPORTED;
+    case 12: VA_TILE(1, 2);
+    case 22: VA_TILE(2, 2);
+    case 42: VA_TILE(4, 2);
+    case 14: VA_TILE(1, 4);
+    case 24: VA_TILE(2, 4);
+    default: return VA_EUNSUPPORTED;
+  }
+#undef VA_TILE
+}
+
+}  // namespace
+
+int launch_splitkv_tile(const FwdParams& fp, int d, int hpc, int nrg, dim3 grid, hipStream_t st) {
+  if (d == 128) return launch_d<128>(fp, hpc, nrg, grid, st);
+  if (d == 256) return launch_d<256>(fp, hpc, nrg, grid, st);
+  return VA_EUNSUPPORTED;
+}
+
+}  // namespace va

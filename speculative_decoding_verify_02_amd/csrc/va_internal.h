@@ -20,7 +20,10 @@ constexpr int kWaves = 4;       // waves per split-KV workgroup
 constexpr int kMaxRows = 128;   // G*D rows one workgroup can hold
 
 // Everything the kernels need, resolved on the host from verify_attn_args.
+enum KernelKind { kGeneric = 0, kTile = 1, kMlaFp8 = 2 };
+
 struct Plan {
+  int kind;         // which split-KV kernel serves the call (KernelKind)
   int rows;         // G * D query rows per KV head
   int group;        // G
   int rt;           // 16-row MFMA tiles per wave (1 or 2)
@@ -52,14 +55,18 @@ struct FwdParams {
   float v_scale;
 };
 
-// Validates args (host only) and fills the plan.  Returns a VA_ status.
-int make_plan(const verify_attn_args* a, Plan* plan);
+// Validates args (host only) and fills the plan.  Returns a VA_ status.  Pointer
+// checks (null, alignment) are skipped when check_pointers is false.
+int make_plan(const verify_attn_args* a, Plan* plan, bool check_pointers);
 
 // Kernel launchers (one per translation unit).
 int launch_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int32_t batch,
                        int lg_page, int32_t max_pages, int32_t* block_table, int32_t* kv_lens,
                        hipStream_t stream);
 int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t stream);
+// bf16 heads with qk_dim = v_dim in {128, 256}: whole-slot-row tiles shared by
+// hpc heads x nrg row groups.
+int launch_splitkv_tile(const FwdParams& fp, int d, int hpc, int nrg, dim3 grid, hipStream_t stream);
 // fp8 MLA heads (qk_dim 576, v_dim 512 = first 512 of the K row), <= 64 rows per head.
 int launch_splitkv_mla_fp8(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t stream);
 int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t stream);

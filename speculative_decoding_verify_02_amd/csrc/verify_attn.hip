@@ -35,21 +35,19 @@ int max_attended_prefix(int max_prefix_len, int window_left) {
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Split heuristic.  A split is one workgroup streaming `chunk` prefix tokens of one
-// (sequence, KV head).  Workgroups are sized so the chip sees several rounds of
-// them (good balance for ragged lengths) while each still streams enough bytes
-// that its fp32 partial (rows x (v_dim+1) x 4 B, written once and read once by
-// the combine) stays a few percent of its KV bytes.
-int heuristic_splits(int batch, int hkv, int max_leff, int cus) {
-  if (max_leff <= 0) return 1;
-  const long long units = (long long)batch * hkv;
-  const long long target_wgs = 16LL * cus;
-  long long chunk = (units * max_leff + target_wgs - 1) / target_wgs;
-  if (chunk < 256) chunk = 256;
-  if (chunk > 2048) chunk = 2048;
-  chunk = round_up((int)chunk, 128);
-  int s = (int)((max_leff + chunk - 1) / chunk);
-  return s < 1 ? 1 : s;
+// Split heuristic.  A split is one workgroup streaming `chunk` prefix tokens of its
+// KV heads; `per_cu` workgroups fit on a compute unit at once.  One full round of
+// workgroups across the chip (per_cu x CUs) measured best: each workgroup streams
+// long runs, and the fp32 partial it writes (rows x (v_dim+1) x 4 B per head) stays
+// small beside its KV bytes.  Chunks stay >= 128 tokens.
+int heuristic_splits(int batch, int head_groups, int max_leff, int cus, int per_cu) {
+  const long long units = (long long)batch * head_groups;
+  if (max_leff <= 0 || units <= 0) return 1;
+  const long long target = (long long)cus * per_cu;
+  long long s = (target + units - 1) / units;
+  const long long s_max = (max_leff + 127) / 128;
+  if (s > s_max) s = s_max;
+  return s < 1 ? 1 : (int)s;
 }
 
 }  // namespace
@@ -70,7 +68,7 @@ int device_cu_count() {
   return cache[dev];
 }
 
-int make_plan(const verify_attn_args* a, Plan* p) {
+int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
   if (!a || a->struct_size != (int32_t)sizeof(verify_attn_args)) return VA_EINVAL;
   if (a->batch < 0 || a->draft_len < 1 || a->hq < 1 || a->hkv < 1 || a->max_prefix_len < 0 ||
       a->num_splits < 0 || a->window_left < -1 || a->max_pages_per_seq < 1)
@@ -89,8 +87,8 @@ int make_plan(const verify_attn_args* a, Plan* p) {
   if (rows > kMaxRows) return VA_EUNSUPPORTED;
 
   if (a->batch > 0) {
-    if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->prefix_lens ||
-        !a->workspace || !a->out)
+    if (check_pointers && (!a->q || !a->k_cache || !a->v_cache || !a->block_table ||
+                           !a->prefix_lens || !a->workspace || !a->out))
       return VA_EINVAL;
     const int eb = a->kv_dtype == VA_KV_FP8_E4M3FN ? 1 : 2;
     // 16-byte vector loads of q / K / V rows need 16-byte aligned rows
@@ -111,21 +109,49 @@ int make_plan(const verify_attn_args* a, Plan* p) {
 
   p->group = group;
   p->rows = rows;
-  p->rt = (rows <= 16) ? 1 : (a->v_dim <= 256 ? 2 : 1);
-  const int tiles = (rows + 15) / 16;
-  const int groups = (tiles + p->rt - 1) / p->rt;
-  p->nrg = groups <= 1 ? 1 : (groups <= 2 ? 2 : (groups <= 4 ? 4 : 0));
-  if (p->nrg == 0) return VA_EUNSUPPORTED;
-  // the remaining waves of a workgroup cover more KV heads of the same tokens, then
-  // interleave tokens of one head
-  const int free_waves = kWaves / p->nrg;
-  p->hpc = a->hkv >= free_waves ? free_waves : (a->hkv >= 2 && free_waves >= 2 ? 2 : 1);
-  p->ntl = free_waves / p->hpc;
+  const bool fp8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
+  int head_groups = a->hkv, per_cu = 1;
+  if (fp8 && a->qk_dim == 576 && rows <= 64) {
+    p->kind = kMlaFp8;                      // one workgroup per (head, split), 4 row-group waves
+    p->rt = 1;
+    p->nrg = 4;
+    p->ntl = 1;
+    p->hpc = 1;
+  } else if (!fp8 && a->qk_dim == 256 && a->v_dim == 256 && rows <= 64) {
+    // wide bf16 heads: whole-slot-row tiles (d = 128 streams better per wave)
+    p->kind = kTile;
+    p->rt = 1;
+    p->nrg = (rows + 15) / 16;
+    if (p->nrg == 3) p->nrg = 4;
+    p->ntl = 1;
+    const int max_hpc = (a->qk_dim == 256 ? 4 : 8) / p->nrg;
+    p->hpc = 1;
+    while (p->hpc * 2 <= max_hpc && a->hkv % (p->hpc * 2) == 0) p->hpc *= 2;
+    head_groups = a->hkv / p->hpc;
+    // two workgroups share a CU when both LDS tile pairs fit (16 tokens x (hpc x 512 B
+    // + 16) x 4 buffers <= 80 KB) and the 16-row waves stay within 256 registers
+    const int tile_lds = 16 * (p->hpc * 2 * a->qk_dim + 16) * 4;
+    per_cu = (tile_lds <= 80 * 1024 && p->nrg >= 2) ? 2 : 1;
+  } else {
+    p->kind = kGeneric;
+    p->rt = (rows <= 16) ? 1 : (a->v_dim <= 256 ? 2 : 1);
+    const int tiles = (rows + 15) / 16;
+    const int groups = (tiles + p->rt - 1) / p->rt;
+    p->nrg = groups <= 1 ? 1 : (groups <= 2 ? 2 : (groups <= 4 ? 4 : 0));
+    if (p->nrg == 0) return VA_EUNSUPPORTED;
+    // the remaining waves of a workgroup cover more KV heads of the same tokens, then
+    // interleave tokens of one head
+    const int free_waves = kWaves / p->nrg;
+    p->hpc = a->hkv >= free_waves ? free_waves : (a->hkv >= 2 && free_waves >= 2 ? 2 : 1);
+    p->ntl = free_waves / p->hpc;
+    head_groups = (a->hkv + p->hpc - 1) / p->hpc;
+    per_cu = (a->qk_dim == 128 && p->rt == 1) ? 2 : 1;
+  }
   p->lg_page = ilog2(a->page_size);
   p->max_leff = max_attended_prefix(a->max_prefix_len, a->window_left);
-  p->splits = a->num_splits > 0
-                  ? a->num_splits
-                  : heuristic_splits(a->batch, a->hkv, p->max_leff, device_cu_count());
+  p->splits = a->num_splits > 0 ? a->num_splits
+                                 : heuristic_splits(a->batch, head_groups, p->max_leff,
+                                                    device_cu_count(), per_cu);
   p->chunk = p->max_leff > 0 ? round_up((p->max_leff + p->splits - 1) / p->splits, kTokBlock)
                              : kTokBlock;
   p->ws_o_floats = (int64_t)a->batch * a->hkv * p->splits * rows * a->v_dim;
@@ -157,18 +183,17 @@ int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int3
   return (int64_t)batch * hkv * num_splits * rows * ((int64_t)v_dim + 1) * 4;
 }
 
-int32_t verify_attn_num_splits(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
-                               int32_t v_dim, int32_t max_prefix_len, int32_t window_left) {
-  if (batch < 0 || hkv < 1 || hq < 1 || hq % hkv || draft_len < 1 || v_dim < 1 ||
-      max_prefix_len < 0 || window_left < -1)
-    return -1;
-  return va::heuristic_splits(batch, hkv, va::max_attended_prefix(max_prefix_len, window_left),
-                              va::device_cu_count());
+int32_t verify_attn_num_splits(const verify_attn_args* args) {
+  va::Plan p;
+  if (!args) return -1;
+  verify_attn_args a = *args;
+  a.num_splits = 0;  // the heuristic's choice, whatever the caller asked for
+  return va::make_plan(&a, &p, /*check_pointers=*/false) == VA_OK ? p.splits : -1;
 }
 
 int verify_attn_can_handle(const verify_attn_args* args) {
   va::Plan p;
-  return va::make_plan(args, &p);
+  return va::make_plan(args, &p, true);
 }
 
 static int check_workspace(const verify_attn_args* a, const va::Plan& p) {
@@ -179,7 +204,7 @@ static int check_workspace(const verify_attn_args* a, const va::Plan& p) {
 
 int verify_attn_fwd(const verify_attn_args* args, void* stream) {
   va::Plan p;
-  int st = va::make_plan(args, &p);
+  int st = va::make_plan(args, &p, true);
   if (st != VA_OK) return st;
   if ((st = check_workspace(args, p)) != VA_OK) return st;
   // launched even when the host bound says no prefix is attended: a device length
@@ -190,7 +215,7 @@ int verify_attn_fwd(const verify_attn_args* args, void* stream) {
 
 int verify_attn_combine(const verify_attn_args* args, void* stream) {
   va::Plan p;
-  int st = va::make_plan(args, &p);
+  int st = va::make_plan(args, &p, true);
   if (st != VA_OK) return st;
   if ((st = check_workspace(args, p)) != VA_OK) return st;
   if (args->batch == 0) return VA_OK;

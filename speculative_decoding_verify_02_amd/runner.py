@@ -53,12 +53,17 @@ class DeviceProblem:
                                device=device)
         self.lse = torch.empty((p.batch * p.draft_len, p.hq), dtype=torch.float32, device=device)
         ns = p.num_splits if num_splits is None else num_splits
-        self.splits = ns if ns > 0 else binding.verify_attn_num_splits(
-            p.batch, p.hkv, p.hq, p.draft_len, p.v_dim, p.max_prefix_len, p.window_left)
+        self.workspace = None
+        self.calls = [self._make_call(c) for c in range(kv_copies)]
+        self.splits = ns if ns > 0 else binding.verify_attn_num_splits(self.calls[0])
+        if self.splits < 1:
+            raise ValueError(f"arguments rejected (status for {p.name})")
         ws = binding.verify_attn_workspace_bytes(p.batch, p.hkv, p.hq, p.draft_len, p.v_dim,
                                                  self.splits)
         self.workspace = torch.empty((max(ws, 4) + 3) // 4, dtype=torch.float32, device=device)
-        self.calls = [self._make_call(c) for c in range(kv_copies)]
+        for c in self.calls:
+            c.args.num_splits = self.splits
+            binding.set_workspace(c, self.workspace)
 
     def _make_call(self, copy: int) -> binding.VerifyCall:
         p = self.p
@@ -68,7 +73,7 @@ class DeviceProblem:
             draft_len=p.draft_len, page_size=p.page_size, sm_scale=p.sm_scale,
             max_prefix_len=p.max_prefix_len, out=self.out, workspace=self.workspace,
             lse=self.lse, kv_dtype=p.kv_dtype, k_scale=p.k_scale, v_scale=p.v_scale,
-            window_left=p.window_left, num_splits=self.splits, qk_dim=p.qk_dim, v_dim=p.v_dim)
+            window_left=p.window_left, num_splits=0, qk_dim=p.qk_dim, v_dim=p.v_dim)
 
     def build_block_table(self, stream=None):
         binding.verify_attn_build_block_table(self.kv_indptr, self.kv_indices, self.p.page_size,

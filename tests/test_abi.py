@@ -136,10 +136,17 @@ def test_block_table_arguments():
 def test_host_helpers():
     assert B.verify_attn_workspace_bytes(1, 1, 1, 1, 128, 0) == -1
     assert B.verify_attn_workspace_bytes(1, 2, 3, 1, 128, 1) == -1     # hq % hkv
-    for args in [(32, 8, 32, 4, 128, 32768, -1), (16, 4, 32, 4, 256, 65536, 4096),
-                 (64, 1, 16, 4, 512, 8192, -1), (1, 2, 8, 4, 128, 0, -1)]:
-        s = B.verify_attn_num_splits(*args)
-        assert s >= 1
-    assert B.verify_attn_num_splits(1, 1, 1, 1, 128, -5, -1) == -1
+    lib = B.load()
+    for kw in [dict(), dict(max_prefix_len=0), dict(batch=0, max_prefix_len=70000),
+               dict(qk_dim=576, v_dim=512, hq=16, hkv=1, kv_dtype=B.VA_KV_FP8_E4M3FN,
+                    k_scale=0.05, v_scale=0.05, k_stride_slot=576, k_stride_head=576,
+                    v_stride_slot=576, v_stride_head=576),
+               dict(num_splits=3)]:
+        s = lib.verify_attn_num_splits(ctypes.byref(fake_args(**kw)))
+        assert s >= 1, kw
+    # host-only sizing query: pointers may still be unset
+    assert lib.verify_attn_num_splits(ctypes.byref(fake_args(workspace=None, q=None, out=None))) >= 1
+    assert lib.verify_attn_num_splits(ctypes.byref(fake_args(max_prefix_len=-5))) == -1
+    assert lib.verify_attn_num_splits(ctypes.byref(fake_args(hq=7))) == -1
     for st in range(6):
         assert isinstance(B.strerror(st), str)
