@@ -56,11 +56,51 @@ def traffic_for(workload: str, src_hash: str):
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source: a recorded traffic figure is valid only for it."""
     h = hashlib.sha256()
-    for name in ("splitkv_fwd.hip", "va_internal.h", "verify_attn.hip"):
-        with open(os.path.join(ROOT, "speculative_decoding_verify_02_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "speculative_decoding_verify_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
     return h.hexdigest()
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int, workload: str,
+                 kernel_key: str = "splitkv") -> dict:
+    """HBM bytes per split-KV launch from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, in KiB per dispatch).  Each counter is scaled by what it reads for the
+    plain device copy of `copy_mib` MiB that --copy-calibration-mib issues last: the
+    copy reads and writes exactly that many bytes."""
+    out = {"workload": workload, "kernel_source_sha256": kernel_source_hash(),
+           "copy_calibration_bytes": copy_mib << 20}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        copies = [(d, v) for (d, name), v in per.items() if "copyBuffer" in name]
+        kern = [v for (d, name), v in per.items() if kernel_key in name]
+        if not copies or not kern:
+            raise SystemExit(f"{path}: no copy or {kernel_key} dispatches")
+        copy_kib = max(copies)[1]             # the calibration copy is the last copy issued
+        factor = (copy_mib << 20) / (copy_kib * 1024.0)
+        mean_kib = sum(kern) / len(kern)
+        bytes_per_launch = mean_kib * 1024.0 * factor
+        out[counter] = {"kernel_mean_kib": round(mean_kib, 1), "copy_kib": round(copy_kib, 1),
+                        "scale": round(factor, 4), "bytes_per_launch": round(bytes_per_launch)}
+        total += bytes_per_launch
+    out["hbm_bytes_per_launch"] = round(total)
+    return out
 
 
 def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
@@ -166,7 +206,22 @@ def main():
     ap.add_argument("--all-configs", action="store_true", help="also time the other large workloads")
     ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, issue one plain device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 counter CSVs")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        from speculative_decoding_verify_02_amd import workloads as W
+        name = W.CONFIG_NAMES[args.config]
+        rec = traffic_from(args.traffic_from[0], args.traffic_from[1],
+                           args.copy_calibration_mib or 1024, name)
+        path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for "
@@ -200,6 +255,16 @@ def main():
                 "fwd_pct_of_peak": round(100 * r["fwd_gbs"] / HBM_PEAK_GBS, 2),
                 "kernels_pct_of_peak": round(100 * r["kernels_gbs"] / HBM_PEAK_GBS, 2),
                 "splits": r["splits"], "kv_copies": r["copies"]}
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 19     # bf16 elements
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB issued")
+        del src, dst
 
     src_hash = kernel_source_hash()
     p = head["p"]

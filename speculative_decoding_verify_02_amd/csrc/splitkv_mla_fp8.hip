@@ -125,11 +125,11 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
         raw = *reinterpret_cast<const u32x4*>(P.q + (int64_t)(b * P.draft + i) * P.q_srow +
                                               (int64_t)(g * P.group + hh) * P.q_shead + 16 * ch);
       }
-      float x[8];
+      float x[8];  // q elements, saturated to the e4m3 range (+-448)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(raw[e] << 16);
-        x[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+        x[2 * e] = fminf(fmaxf(__uint_as_float(raw[e] << 16), -448.f), 448.f);
+        x[2 * e + 1] = fminf(fmaxf(__uint_as_float(raw[e] & 0xffff0000u), -448.f), 448.f);
       }
       uint32_t hi[2], lo[2];
 #pragma unroll
