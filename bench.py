@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--all-configs]
 
 One step = the whole path on one batch: block-table scatter, split-KV pass over
-the prefix, combine with the draft block.  Inputs are seeded synthetic workloads
+the prefix and the causal draft keys, log-sum-exp combine.  Inputs are seeded synthetic workloads
 resident in HBM before timing starts.  Prints ONE JSON line:
 
   value          KV-read GB/s of the whole step (algorithmic bytes / step time)
@@ -32,15 +32,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 CACHE_BYTES = 256 << 20
-
-
-def prefix_kv_bytes(p) -> int:
-    """Algorithmic bytes of the split-KV launch: attended prefix tokens only (the
-    draft tokens are read by the combine)."""
-    from speculative_decoding_verify_02_amd import workloads as W
-    per_tok = p.hkv * (p.qk_dim + (0 if p.v_aliases_k else p.v_dim)) * p.elem_bytes
-    toks = sum(W.visible_token_count(int(L), 0, p.window_left) for L in p.prefix_lens)
-    return int(toks) * per_tok
 
 
 def traffic_for(workload: str, src_hash: str):
@@ -114,7 +105,7 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
     p = W.make_config(idx)
     log(f"[bench] config {idx} {p.name}: inputs drawn in {time.time() - t0:.1f}s")
     kv_bytes = W.algorithmic_kv_bytes(p)
-    fwd_bytes = prefix_kv_bytes(p)
+    fwd_bytes = kv_bytes  # the split-KV pass reads every visible key, draft keys included
     copies = 1 if kv_bytes > 2 * CACHE_BYTES else 3
     dp = DeviceProblem(p, device="cuda", num_splits=splits, kv_copies=copies)
     torch.cuda.synchronize()
@@ -143,11 +134,15 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
     bt_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     comb_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    # fwd + combine per step, the verify-attention call time
+    call_us = sorted(e[1].elapsed_time(e[3]) * 1e3 for e in ev)
+    pct = lambda f: call_us[min(len(call_us) - 1, int(f * (len(call_us) - 1) + 0.5))]
     ms_per_step = wall * 1e3 / steps
     rec = dict(
         idx=idx, name=p.name, p=p, kv_bytes=kv_bytes, fwd_bytes=fwd_bytes,
         ms_per_step=ms_per_step, bt_us=bt_ms * 1e3, fwd_us=fwd_ms * 1e3, comb_us=comb_ms * 1e3,
         splits=dp.splits, copies=copies,
+        call_us={"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2)},
         step_gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
         fwd_gbs=fwd_bytes / (fwd_ms * 1e-3) / 1e9,
         kernels_gbs=kv_bytes / ((bt_ms + fwd_ms + comb_ms) * 1e-3) / 1e9,
@@ -254,6 +249,9 @@ def main():
                 "step_gbs": round(r["step_gbs"], 1), "fwd_gbs": round(r["fwd_gbs"], 1),
                 "fwd_pct_of_peak": round(100 * r["fwd_gbs"] / HBM_PEAK_GBS, 2),
                 "kernels_pct_of_peak": round(100 * r["kernels_gbs"] / HBM_PEAK_GBS, 2),
+                "call_us": r["call_us"],
+                "call_pct_of_peak": round(100 * r["kv_bytes"] / (r["call_us"]["median"] * 1e-6)
+                                          / 1e9 / HBM_PEAK_GBS, 2),
                 "splits": r["splits"], "kv_copies": r["copies"]}
 
     if args.copy_calibration_mib > 0:
@@ -293,6 +291,10 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 q/k/v, shuffled page table)",
         "config": dict(workload_config(p), splits=head["splits"], kv_copies=head["copies"],
                        kv_mb=round(head["kv_bytes"] / 1e6, 2)),
+        # verify_attn_fwd + verify_attn_combine per call (HIP events), and its share of peak
+        "call_us": head["call_us"],
+        "call_pct_of_peak": round(100 * head["kv_bytes"] / (head["call_us"]["median"] * 1e-6)
+                                  / 1e9 / HBM_PEAK_GBS, 2),
         "kernel_us": {"block_table": round(head["bt_us"], 2), "splitkv_fwd": round(head["fwd_us"], 2),
                       "combine": round(head["comb_us"], 2)},
         "roofline": roof,

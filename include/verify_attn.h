@@ -13,13 +13,16 @@
  *   "Code Review" on the target-verify unified-attention call).
  *
  *   The work is split as on PR #27382 ("Motivation", "Modifications"): a
- *   split-KV (flash-decode) pass over the prefix writes one partial output and
- *   log-sum-exp per split (verify_attn_fwd), then a combine merges the partials
- *   with the causal draft-draft block (verify_attn_combine).  The paged cache is
- *   addressed through a 2-D block table built from the token-level
- *   kv_indptr/kv_indices lists (verify_attn_build_block_table; PR #23146 builds
- *   the same table with scatter kernels, and PR #5168 notes that at topk = 1 the
- *   tokens of a page are consecutive, which is what makes the table valid).
+ *   split-KV (flash-decode) pass writes one partial output and log-sum-exp per
+ *   piece of a sequence's keys (verify_attn_fwd), then a combine merges the
+ *   partials by log-sum-exp (verify_attn_combine).  Here the pass also covers
+ *   the small causal draft-draft block: the D draft keys are the last keys of a
+ *   sequence and the per-row causal bound t <= p masks them, so the combine is a
+ *   pure merge.  The paged cache is addressed through a 2-D block table built
+ *   from the token-level kv_indptr/kv_indices lists
+ *   (verify_attn_build_block_table; PR #23146 builds the same table with scatter
+ *   kernels, and PR #5168 notes that at topk = 1 the tokens of a page are
+ *   consecutive, which is what makes the table valid).
  *
  * Conventions for every entry point
  *   - Pointers named in a verify_attn_args or passed to build_block_table are
@@ -79,8 +82,11 @@ typedef struct verify_attn_args {
     int32_t window_left;    /* -1: no window; W >= 0: keep keys t >= p - W              */
     int32_t max_prefix_len; /* host-side upper bound of prefix_lens[b]; sizes the grid.
                                A larger device value stays correct but runs slower.     */
-    int32_t num_splits;     /* 0: library heuristic (CU count); else split slots per
-                               (sequence, KV head), >= 1                                 */
+    int32_t num_splits;     /* S, partial slots per (sequence, KV head): 0 = library
+                               heuristic (CU count); else >= 1.  The keys of all
+                               sequences are cut into equal ranges, one per
+                               workgroup, and S bounds how many ranges one sequence
+                               may span (1 = one workgroup per sequence).           */
 
     /* q: [B*D, hq, qk_dim] bf16                                                        */
     const void* q;
@@ -134,22 +140,28 @@ int verify_attn_build_block_table(const int32_t* kv_indptr, const int32_t* kv_in
                                   int32_t* block_table, int32_t* kv_lens, void* stream);
 
 /*
- * Split-KV pass over the prefix (PR #27382 stage 1): for every (sequence, KV head,
- * split) the prefix keys of the split's chunk are gathered through the block
- * table and attended by all G*D query rows of that KV head; the split's partial
- * output (normalised within the split, times v_scale) and its LSE go to the
- * workspace.  Splits cut [max(0, L_b - W), L_b) (or [0, L_b) without a window)
- * into chunks of equal size.  Draft keys are left to verify_attn_combine.
+ * Split-KV pass (PR #27382 stage 1).  Sequence b owns the keys [lo_b, L_b + D):
+ * its attended prefix (lo_b = max(0, L_b - W) with a window, else 0) and its D
+ * draft keys.  The keys of all sequences, laid end to end, are cut into equal
+ * ranges of about T / (workgroups) keys (at least ceil(max len / (S - 1))); a
+ * range is split at sequence ends into pieces, and each piece is gathered through
+ * the block table and attended by all G*D query rows of each KV head, row i
+ * seeing keys p - W <= t <= p (p = L_b + i).  Piece k of sequence b writes its
+ * partial output (normalised within the piece, times v_scale) and LSE to slot k
+ * of the workspace, and the number of pieces of b is recorded there too.  The
+ * ranges are derived on the device from prefix_lens; only host scalars size the
+ * grid, and a sequence never spans more than S slots.
  * Errors: VA_EINVAL / VA_EUNSUPPORTED / VA_EWORKSPACE as for can_handle plus a
  * workspace check; VA_EHIP if the launch fails.
  */
 int verify_attn_fwd(const verify_attn_args* args, void* stream);
 
 /*
- * Combine (PR #27382 stage 2): per query row, the causal draft-draft block (draft
- * keys L_b .. L_b+i, within the window) forms one more partial, and all partials
- * are merged by log-sum-exp into out (bf16) and lse (fp32, optional).
- * Must follow verify_attn_fwd with the same args on the same stream.
+ * Combine (PR #27382 stage 2): per query row, the partials of the sequence's
+ * pieces are merged by log-sum-exp into out (bf16) and lse (fp32, optional).  A
+ * piece in which the row sees no key carries LSE = -inf and weight 0; every row
+ * sees at least its own draft key.  Must follow verify_attn_fwd with the same
+ * args on the same stream.
  */
 int verify_attn_combine(const verify_attn_args* args, void* stream);
 
@@ -171,8 +183,9 @@ int verify_attn_can_handle(const verify_attn_args* args);
 int32_t verify_attn_num_splits(const verify_attn_args* args);
 
 /*
- * Workspace bytes needed for num_splits split slots (>= 1):
- *   batch * hkv * num_splits * (hq/hkv * draft_len) * (v_dim + 1) * 4.
+ * Workspace bytes needed for num_splits partial slots (>= 1):
+ *   (batch * hkv * num_splits * (hq/hkv * draft_len) * (v_dim + 1) + batch) * 4
+ * (partial outputs, partial LSEs, one int32 piece count per sequence).
  * Host only.  Returns -1 on invalid input.  Size it once for the largest batch
  * and reuse it (PR #27382 review: scratch keyed on a stable max batch, fixed
  * addresses for graph replay).

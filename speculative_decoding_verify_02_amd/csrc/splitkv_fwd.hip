@@ -5,10 +5,11 @@
 // parallel programs, each writing a partial output and log-sum-exp that a second
 // stage merges.  This is the gfx950 design of that first stage:
 //
-//   workgroup = (head group, split s, sequence b), 4 waves of 64 lanes.
+//   workgroup = (head group, key range y), 4 waves of 64 lanes; the range is cut
+//   at sequence ends into pieces (see PieceWalk), each attended in turn.
 //   All G*D query rows of a KV head form the dense M dimension (16/32/64 rows).
 //   The 4 waves cover HPC KV heads x NRG row groups (16*RT rows each) x NTL token
-//   lanes; token lanes of one (head, row group) interleave the split's blocks and
+//   lanes; token lanes of one (head, row group) interleave the piece's blocks and
 //   merge through LDS at the end.  The grid runs head groups fastest, so the heads
 //   of one token range are read at about the same time (DRAM locality).
 //
@@ -28,12 +29,13 @@
 //      data movement) and V^T's A operand is a transpose inside the lane's
 //      registers (the column permutation is undone when the partial is written).
 // For d = 128 the next block's K/V loads are in flight while a block computes.
-// The last wave of each (head, row group) writes the split's partial O (normalised,
+// The last wave of each (head, row group) writes the piece's partial O (normalised,
 // times v_scale) and LSE (natural log) to the workspace.
 //
-// Masking: the tail of a split and, with a left window W, keys t < L + i - W of
-// row i.  Masked scores are set to -inf by selection; masked token loads are
-// clamped to the split's last real token so no load leaves the sequence.
+// Masking: row i (position p = L + i) keeps keys p - W <= t <= p, so later draft
+// keys are causal-masked and, with a left window W, old prefix keys too.  Masked
+// scores are set to -inf by selection; token loads past the piece are clamped to
+// its last real token so no load leaves the sequence.
 
 #include <limits.h>
 #include <math.h>
@@ -91,7 +93,7 @@ struct KVRegs {
   uint32_t v[4 * G::TB / 16][G::VW];  // V groups of the lane's score-slot tokens
 };
 
-// Slot of token t0 + (lane % tb), clamped to the split's last token: one page-id
+// Slot of token t0 + (lane % tb), clamped to the piece's last token: one page-id
 // load per lane covers a whole block; other lanes read it with ds_bpermute.
 __device__ __forceinline__ int lane_slot(const int32_t* bt_row, int t0, int t_last, int lane,
                                          int tb, int lg, int pmask) {
@@ -155,8 +157,9 @@ struct RowState {
 template <class G, bool FP8, int RT, int DV>
 __device__ __forceinline__ void compute_block(const uint8_t* tile, const KVRegs<G>& R,
                                               const bf16x8 (&qB)[RT][G::KSTEPS],
-                                              const int (&row_lo)[RT], RowState<DV, RT>& st,
-                                              int t0, int t_end, float c_log2, int n, int j) {
+                                              const int (&row_lo)[RT], const int (&row_hi)[RT],
+                                              RowState<DV, RT>& st, int t0, float c_log2, int n,
+                                              int j) {
   constexpr int TT = G::TB / 16;
   constexpr int NS = 4 * TT;  // scores per lane per row tile
   constexpr int CPL = G::CPL;
@@ -202,7 +205,7 @@ __device__ __forceinline__ void compute_block(const uint8_t* tile, const KVRegs<
 #pragma unroll
     for (int e = 0; e < NS; ++e) {
       const int t = t0 + 16 * (e >> 2) + 4 * j + (e & 3);
-      const bool ok = (t < t_end) && (t >= row_lo[rt]);
+      const bool ok = (t >= row_lo[rt]) && (t <= row_hi[rt]);
       const float v = ok ? sacc[e >> 2][rt][e & 3] * c_log2 : -INFINITY;
       sc[e] = v;
       bmax = fmaxf(bmax, v);
@@ -292,22 +295,28 @@ void splitkv_fwd_kernel(FwdParams P) {
   const int rg = (wave / NTL) % NRG;
   const int tl = wave % NTL;
   const int g = blockIdx.x * HPC + hc;     // KV head of this wave
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
   const bool head_ok = g < P.hkv;          // the last head group may be partial
+  PieceWalk pw;
+  if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
+  const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
+  const uint8_t* vg = P.v + (int64_t)g * P.v_shead;
+  uint8_t* tile = s_tile[wave];
+  const int lg = P.lg_page;
+  const int pmask = (1 << lg) - 1;
 
-  // a2: this split's slice of the attended prefix [lo, L)
-  const int L = P.prefix_lens[b];
-  const int lo = P.window >= 0 ? max(0, L - P.window) : 0;
-  const int nsplit = (L - lo + P.chunk - 1) / P.chunk;
-  if (s >= nsplit) return;  // uniform over the workgroup, before any barrier
-  const int t_begin = lo + s * P.chunk;
-  const int t_end = (s == P.splits - 1) ? L : min(L, t_begin + P.chunk);
+  do {
+  const Piece pc = pw.piece(P);
+  const int b = pc.b;
+  const int L = pc.L;
+  const int t_begin = pc.t0, t_end = pc.t1;
   const int nblk = head_ok ? (t_end - t_begin + TB - 1) / TB : 0;
+  const int t_last = t_end - 1;
+  if (pc.count > 0 && blockIdx.x == 0 && threadIdx.x == 0) P.counts[b] = pc.count;
 
   // Q^T as the B operand: lane holds row n of each row tile, 8 consecutive k-slots.
+  // Keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys).
   bf16x8 qB[RT][KSTEPS];
-  int row_lo[RT];
+  int row_lo[RT], row_hi[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = (rg * RT + rt) * 16 + n;
@@ -315,6 +324,7 @@ void splitkv_fwd_kernel(FwdParams P) {
     const int i = rv ? row / P.group : 0;
     const int hh = rv ? row % P.group : 0;
     row_lo[rt] = P.window >= 0 ? L + i - P.window : INT_MIN;
+    row_hi[rt] = rv ? min(t_last, L + i) : -1;
     const uint8_t* qp =
         P.q + (int64_t)(b * P.draft + i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
@@ -337,12 +347,6 @@ void splitkv_fwd_kernel(FwdParams P) {
   }
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-  const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
-  const uint8_t* vg = P.v + (int64_t)g * P.v_shead;
-  uint8_t* tile = s_tile[wave];
-  const int lg = P.lg_page;
-  const int pmask = (1 << lg) - 1;
-  const int t_last = t_end - 1;
   auto t0_of = [&](int bk) { return t_begin + bk * TB; };
 
   // a3: this wave's blocks are tl, tl+NTL, ...
@@ -360,13 +364,13 @@ void splitkv_fwd_kernel(FwdParams P) {
         const int b1 = blk + NTL, b2 = blk + 2 * NTL;
         if (b1 < nblk) load_block<G>(Bk, sl_next, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
         if (b2 < nblk) sl_after = lane_slot(bt_row, t0_of(b2), t_last, lane, TB, lg, pmask);
-        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, st, t0_of(blk), t_end, P.c_log2, n, j);
+        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, row_hi, st, t0_of(blk), P.c_log2, n, j);
         if (b1 >= nblk) break;
         stage_k<G>(Bk, tile, lane);
         const int b3 = blk + 3 * NTL;
         if (b2 < nblk) load_block<G>(A, sl_after, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
         if (b3 < nblk) sl_next = lane_slot(bt_row, t0_of(b3), t_last, lane, TB, lg, pmask);
-        compute_block<G, FP8, RT, DV>(tile, Bk, qB, row_lo, st, t0_of(b1), t_end, P.c_log2, n, j);
+        compute_block<G, FP8, RT, DV>(tile, Bk, qB, row_lo, row_hi, st, t0_of(b1), P.c_log2, n, j);
         if (b2 >= nblk) break;
         stage_k<G>(A, tile, lane);
         blk = b2;
@@ -378,7 +382,7 @@ void splitkv_fwd_kernel(FwdParams P) {
         load_block<G>(A, sl, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
         if (blk + NTL < nblk) sl = lane_slot(bt_row, t0_of(blk + NTL), t_last, lane, TB, lg, pmask);
         stage_k<G>(A, tile, lane);
-        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, st, t0_of(blk), t_end, P.c_log2, n, j);
+        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, row_hi, st, t0_of(blk), P.c_log2, n, j);
       }
     }
   }
@@ -443,15 +447,14 @@ void splitkv_fwd_kernel(FwdParams P) {
       }
       __syncthreads();
     }
-    if (tl != NTL - 1) return;
   }
-  if (!head_ok) return;
 
-  // write the split's partial.  Lane holds row n; for group c and r = 0..3 the
-  // columns c*CG + EPG*(4*j + r) + [0, EPG).
-  const int64_t split_id = ((int64_t)b * P.hkv + g) * P.splits + s;
+  // write the piece's partial (the last token lane of each (head, row group)).
+  // Lane holds row n; for group c and r = 0..3 the columns c*CG + EPG*(4*j + r) + [0, EPG).
+  const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
+    if (tl != NTL - 1 || !head_ok) break;
     const int row = (rg * RT + rt) * 16 + n;
     if (row >= P.rows) continue;
     const float l = l_run[rt];
@@ -473,6 +476,7 @@ void splitkv_fwd_kernel(FwdParams P) {
     if (j == 0)
       P.part_lse[split_id * P.rows + row] = l > 0.f ? (m_run[rt] + log2f(l)) * kLn2 : -INFINITY;
   }
+  } while (pw.next(P));
 }
 
 namespace {
@@ -539,20 +543,23 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.prefix_lens = a->prefix_lens;
   fp.part_o = a->workspace;
   fp.part_lse = a->workspace + p.ws_o_floats;
+  fp.counts = reinterpret_cast<int32_t*>(a->workspace + p.ws_cnt_floats);
+  fp.batch = a->batch;
   fp.hkv = a->hkv;
   fp.group = p.group;
   fp.draft = a->draft_len;
   fp.rows = p.rows;
   fp.lg_page = p.lg_page;
   fp.window = a->window_left;
-  fp.splits = p.splits;
-  fp.chunk = p.chunk;
+  fp.slots = p.slots;
+  fp.min_q = p.min_q;
   fp.c_log2 = a->sm_scale * a->k_scale * kLog2e;
   fp.v_scale = a->v_scale;
-  if (p.kind == kMlaFp8) return launch_splitkv_mla_fp8(fp, p, dim3(a->hkv, p.splits, a->batch), st);
-  if (p.kind == kTile)
-    return launch_splitkv_tile(fp, a->qk_dim, p.hpc, p.nrg, dim3(a->hkv / p.hpc, p.splits, a->batch), st);
-  const dim3 grid((a->hkv + p.hpc - 1) / p.hpc, p.splits, a->batch);
+  // grid: x = head groups (fastest, so the heads of one key range are read together),
+  // y = key ranges of the balanced partition
+  const dim3 grid(p.hg, p.nwy, 1);
+  if (p.kind == kMlaFp8) return launch_splitkv_mla_fp8(fp, p, grid, st);
+  if (p.kind == kTile) return launch_splitkv_tile(fp, a->qk_dim, p.hpc, p.nrg, grid, st);
   const bool f8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
   if (a->qk_dim == 128) return f8 ? launch_dims<128, 128, true>(fp, p, grid, st)
                                   : launch_dims<128, 128, false>(fp, p, grid, st);

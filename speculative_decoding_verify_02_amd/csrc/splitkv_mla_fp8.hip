@@ -5,7 +5,7 @@
 // on one GPU's share), so each token costs ~140 kflop: this kernel is built to keep
 // the MFMA pipes busy while streaming the cache.
 //
-//   workgroup = (KV head g, split s, sequence b), 4 waves; wave w owns rows
+//   workgroup = (KV head g, key range y: pieces of sequences), 4 waves; wave w owns rows
 //   16w .. 16w+15.  Blocks of 128 tokens: the workgroup loads a block's K rows
 //   coalesced into registers (the next block's loads are in flight while the
 //   current block computes), stages them in one shared LDS tile, and every wave
@@ -69,7 +69,7 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t x) {
   return r;
 }
 
-// Slots of the block's tokens t0 + lane and t0 + 64 + lane (clamped to the split).
+// Slots of the block's tokens t0 + lane and t0 + 64 + lane (clamped to the piece).
 __device__ __forceinline__ void block_slots(const int32_t* bt_row, int t0, int t_last, int lane,
                                             int lg, int pmask, int& sa, int& sb) {
   const int ta = min(t0 + lane, t_last), tb = min(t0 + 64 + lane, t_last);
@@ -80,39 +80,38 @@ __device__ __forceinline__ void block_slots(const int32_t* bt_row, int t0, int t
 // Token of score slot i (0..31) of lane group j: tile i/4, accumulator row 4j + i%4.
 __device__ __forceinline__ int slot_token(int j, int i) { return 16 * (i >> 2) + 4 * j + (i & 3); }
 
-}  // namespace
+// LDS of the one workgroup a compute unit holds: the shared K tile and each wave's
+// staged Q rows.
+__shared__ __attribute__((aligned(16))) uint8_t s_tile[kMB * kRS];
+__shared__ __attribute__((aligned(16))) uint8_t s_qtile[kWaves][16 * kQRS];
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-void splitkv_mla_fp8_kernel(FwdParams P) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kMB * kRS];
-  __shared__ __attribute__((aligned(16))) uint8_t qtile[kWaves][16 * kQRS];
-
+// One piece: keys [pc.t0, pc.t1) of sequence pc.b for KV head g -> partial slot
+// pc.slot.  Kept out of line so the piece loop adds no register pressure to it.
+__device__ __noinline__ void mla_piece(const FwdParams& P, const Piece pc, int g) {
+  uint8_t* tile = s_tile;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int j = lane >> 4;
-  const int g = blockIdx.x;
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
-
-  // a2: the split's slice of the attended prefix [lo, L)
-  const int L = P.prefix_lens[b];
-  const int lo = P.window >= 0 ? max(0, L - P.window) : 0;
-  const int nsplit = (L - lo + P.chunk - 1) / P.chunk;
-  if (s >= nsplit) return;  // uniform over the workgroup, before any barrier
-  const int t_begin = lo + s * P.chunk;
-  const int t_end = (s == P.splits - 1) ? L : min(L, t_begin + P.chunk);
+  const int row = wave * 16 + n;
+  const bool rv = row < P.rows;
+  const int row_i = rv ? row / P.group : 0;  // draft index of this lane's row
+  uint8_t* qw = s_qtile[wave];
+  const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
+  const int lg = P.lg_page;
+  const int pmask = (1 << lg) - 1;
+  const int b = pc.b;
+  const int L = pc.L;
+  const int t_begin = pc.t0, t_end = pc.t1;
   const int nblk = (t_end - t_begin + kMB - 1) / kMB;
   const int t_last = t_end - 1;
+  if (pc.count > 0 && g == 0 && tid == 0) P.counts[b] = pc.count;
 
   // this wave's 16 Q rows go to its own LDS rows: for d < 512 as two e4m3 terms
   // (hi = e4m3(q), lo = e4m3(16 (q - hi)), together ~2^-9 relative error, the
   // precision of the bf16 q itself) for the fp8 MFMA, and the 64-wide rope tail
   // d >= 512 as bf16.  Row layout: hi[512] | lo[512] | bf16 tail[64].
-  const int row = wave * 16 + n;
-  const bool rv = row < P.rows;
-  uint8_t* qw = qtile[wave];
   {
 #pragma unroll
     for (int c = 0; c < 16 * (kVRB / 8) / 64; ++c) {       // 16 chunks of 8 values per lane
@@ -163,7 +162,9 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
       *reinterpret_cast<u32x4*>(qw + r * kQRS + 2 * kVRB + 16 * ch) = raw;
     }
   }
-  const int row_lo = (P.window >= 0 && rv) ? L + row / P.group - P.window : INT_MIN;
+  // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
+  const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
+  const int row_hi = rv ? min(t_last, L + row_i) : -1;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[kCT];
@@ -171,9 +172,6 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   for (int ct = 0; ct < kCT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-  const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
-  const int lg = P.lg_page;
-  const int pmask = (1 << lg) - 1;
 
   // coalesced block load: thread chunk q = 256u + tid -> token q / 36, chunk q % 36
   u32x4 kreg[kNLD];
@@ -251,7 +249,7 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int t = t0 + slot_token(j, e);
-      const bool ok = (t < t_end) && (t >= row_lo);
+      const bool ok = (t >= row_lo) && (t <= row_hi);
       const float v = ok ? sacc[e >> 2][e & 3] * P.c_log2 : -INFINITY;
       sc[e] = v;
       bmax = fmaxf(bmax, v);
@@ -316,19 +314,31 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   // each lane summed only its own tokens: total the 4 lanes of the row
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!rv) return;
-  const int64_t split_id = ((int64_t)b * P.hkv + g) * P.splits + s;
-  const float inv = l_run > 0.f ? P.v_scale / (l_run * kPScale) : 0.f;
-  float* po = P.part_o + (split_id * P.rows + row) * kVRB + 4 * j;
+  if (rv) {
+    const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
+    const float inv = l_run > 0.f ? P.v_scale / (l_run * kPScale) : 0.f;
+    float* po = P.part_o + (split_id * P.rows + row) * kVRB + 4 * j;
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) {
-    f32x4 o = oacc[ct];
+    for (int ct = 0; ct < kCT; ++ct) {
+      f32x4 o = oacc[ct];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] *= inv;
-    *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
+      for (int r = 0; r < 4; ++r) o[r] *= inv;
+      *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
+    }
+    if (j == 0)
+      P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
-  if (j == 0)
-    P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void splitkv_mla_fp8_kernel(FwdParams P) {
+  PieceWalk pw;
+  if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
+  do {
+    mla_piece(P, pw.piece(P), blockIdx.x);
+  } while (pw.next(P));
 }
 
 int launch_splitkv_mla_fp8(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {

@@ -4,7 +4,7 @@
 // In the [slot, H_kv, d] layout (the paged view of PR #23146) the K rows of all
 // KV heads of one token are adjacent, and a page of P tokens is P * H_kv * d
 // contiguous elements.  A workgroup therefore takes HPC KV heads of one
-// (sequence, split) and loads each 16-token block cooperatively: every load
+// key range (pieces of sequences) and loads each 16-token block cooperatively: every load
 // instruction reads whole runs of a slot row (all HPC heads), so HBM sees long
 // contiguous reads instead of one head's 256-byte slices.  K and V blocks go to
 // double-buffered LDS tiles (the next block loads while this one computes);
@@ -18,7 +18,7 @@
 //       columns and lane c receives column c of the 4 rows; the lane's own 4
 //       probabilities are the B operand.
 // Waves: HPC heads x NRG row groups (16 rows each).  No merge between waves: each
-// wave owns its (head, rows) for the whole split and writes its partial.
+// wave owns its (head, rows) for the whole piece and writes its partial.
 
 #include <limits.h>
 #include <math.h>
@@ -68,28 +68,29 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   const int rg = wave % NRG;          // row group of that head
   const int g0 = blockIdx.x * HPC;    // first KV head of the workgroup (HPC divides H_kv)
   const int g = g0 + hc;
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
-
-  // a2: this split's slice of the attended prefix [lo, L)
-  const int L = P.prefix_lens[b];
-  const int lo = P.window >= 0 ? max(0, L - P.window) : 0;
-  const int nsplit = (L - lo + P.chunk - 1) / P.chunk;
-  if (s >= nsplit) return;  // uniform over the workgroup, before any barrier
-  const int t_begin = lo + s * P.chunk;
-  const int t_end = (s == P.splits - 1) ? L : min(L, t_begin + P.chunk);
-  const int nblk = (t_end - t_begin + kTB - 1) / kTB;
-  const int t_last = t_end - 1;
-
-  // Q^T operands of this wave's 16 rows: k-step ks holds elements 32ks + 8j + [0, 8)
+  PieceWalk pw;
+  if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
   const int row = rg * 16 + n;
   const bool rv = row < P.rows;
+  const int row_i = rv ? row / P.group : 0;  // draft index of this lane's row
+  const int lg = P.lg_page;
+  const int pmask = (1 << lg) - 1;
+
+  do {
+  const Piece pc = pw.piece(P);
+  const int b = pc.b;
+  const int L = pc.L;
+  const int t_begin = pc.t0, t_end = pc.t1;
+  const int nblk = (t_end - t_begin + kTB - 1) / kTB;
+  const int t_last = t_end - 1;
+  if (pc.count > 0 && blockIdx.x == 0 && tid == 0) P.counts[b] = pc.count;
+
+  // Q^T operands of this wave's 16 rows: k-step ks holds elements 32ks + 8j + [0, 8)
   bf16x8 qB[KS];
   {
-    const int i = rv ? row / P.group : 0;
     const int hh = rv ? row % P.group : 0;
     const uint8_t* qp =
-        P.q + (int64_t)(b * P.draft + i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
+        P.q + (int64_t)(b * P.draft + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
@@ -97,7 +98,9 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
       qB[ks] = as_bf16x8(raw);
     }
   }
-  const int row_lo = (P.window >= 0 && rv) ? L + row / P.group - P.window : INT_MIN;
+  // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
+  const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
+  const int row_hi = rv ? min(t_last, L + row_i) : -1;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[CT];
@@ -105,8 +108,6 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-  const int lg = P.lg_page;
-  const int pmask = (1 << lg) - 1;
   // this thread's load chunks: q = 64*W*u + tid -> token q / CH, head (q % CH) / (RB/16)
   auto lane_slot = [&](int t0) {
     const int t = min(t0 + (lane & (kTB - 1)), t_last);
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * j + r;
-      const bool ok = (t < t_end) && (t >= row_lo);
+      const bool ok = (t >= row_lo) && (t <= row_hi);
       sc[r] = ok ? sacc[r] * P.c_log2 : -INFINITY;
       bmax = fmaxf(bmax, sc[r]);
     }
@@ -212,20 +213,22 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   // each lane summed only its own tokens: total the 4 lanes of the row
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!rv) return;
-  const int64_t split_id = ((int64_t)b * P.hkv + g) * P.splits + s;
-  const float inv = l_run > 0.f ? P.v_scale / l_run : 0.f;
-  // lane holds O[row][16ct + 4j + r], r = 0..3
-  float* po = P.part_o + (split_id * P.rows + row) * D + 4 * j;
+  if (rv) {
+    const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
+    const float inv = l_run > 0.f ? P.v_scale / l_run : 0.f;
+    // lane holds O[row][16ct + 4j + r], r = 0..3
+    float* po = P.part_o + (split_id * P.rows + row) * D + 4 * j;
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    f32x4 o = oacc[ct];
+    for (int ct = 0; ct < CT; ++ct) {
+      f32x4 o = oacc[ct];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] *= inv;
-    *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
+      for (int r = 0; r < 4; ++r) o[r] *= inv;
+      *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
+    }
+    if (j == 0)
+      P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
-  if (j == 0)
-    P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  } while (pw.next(P));
 }
 
 namespace {

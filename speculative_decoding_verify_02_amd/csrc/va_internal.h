@@ -30,11 +30,14 @@ struct Plan {
   int nrg;          // row groups of one KV head (1, 2, 4)
   int ntl;          // token lanes: waves that interleave one (head, row group)'s blocks
   int hpc;          // KV heads per workgroup; hpc * nrg * ntl = 4 waves
+  int hg;           // head groups: workgroups along grid x
   int lg_page;      // log2(page_size)
-  int splits;       // split slots per (sequence, KV head)
-  int chunk;        // prefix tokens per split (multiple of kTokBlock)
-  int max_leff;     // max over sequences of the attended prefix length
-  int64_t ws_o_floats;  // offset of partial LSEs in the workspace (floats)
+  int slots;        // partial slots per (sequence, KV head): the split count S
+  int nwy;          // workgroups along grid y (token ranges)
+  int min_q;        // fewest tokens one workgroup is given
+  int max_leff;     // host bound of the attended prefix length
+  int64_t ws_o_floats;    // offset of partial LSEs in the workspace (floats)
+  int64_t ws_cnt_floats;  // offset of the per-sequence piece counts (int32)
 };
 
 // Split-KV kernel parameters (strides in bytes), resolved from verify_attn_args.
@@ -50,9 +53,152 @@ struct FwdParams {
   const int32_t* prefix_lens;
   float* part_o;
   float* part_lse;
-  int hkv, group, draft, rows, lg_page, window, splits, chunk;
+  int32_t* counts;   // [B] pieces written per sequence
+  int batch, hkv, group, draft, rows, lg_page, window;
+  int slots, min_q;
   float c_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
+};
+
+// ---------------------------------------------------------------------------
+// Work partition of the split-KV pass (device side, identical in every wave).
+//
+// Sequence b owns len_b = (L_b - lo_b) + D keys: its attended prefix [lo_b, L_b)
+// (lo_b = max(0, L_b - W) with a left window W, else 0) and then its D draft keys,
+// which sit in the paged cache right after the prefix.  The sequences' keys are
+// laid end to end (T in all) and cut into ranges of
+//     q = max(ceil(T / nwy), ceil(max_b len_b / (slots - 1)), min_q)
+// keys, range y going to the workgroups of grid row y (one per head group), so
+// every workgroup streams about the same number of keys whatever the length mix.
+// A range is cut at sequence ends into pieces.  Sequence b's pieces come from
+// consecutive rows first_b .. last_b with first_b = floor(cum_b / q) and last_b =
+// floor((cum_b + len_b - 1) / q); the piece of row y writes partial slot
+// y - first_b, and the row holding the last piece records the count.  A sequence
+// spans at most floor((len_b - 1) / q) + 2 <= slots rows, whatever the device
+// lengths are, so the slots never overflow.  With slots == 1 row y takes all of
+// sequence y.  Only host scalars size the grid; lengths are read on the device.
+struct Piece {
+  int b;       // sequence
+  int L;       // its prefix length
+  int t0, t1;  // key positions [t0, t1) of this piece, inside [lo_b, L_b + D)
+  int slot;    // partial slot
+  int count;   // on the sequence's last piece, its number of pieces; else 0
+};
+
+__device__ __forceinline__ int seq_prefix_len(const FwdParams& P, int b) {
+  return max(P.prefix_lens[b], 0);
+}
+
+__device__ __forceinline__ int seq_lo(const FwdParams& P, int L) {
+  return P.window >= 0 ? max(0, L - P.window) : 0;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+struct PieceWalk {
+  int64_t a, e, q, cum;
+  int b, y, len;
+
+  // Finds row y's first piece.  Returns false when the row has no keys.
+  __device__ bool init(const FwdParams& P, int row) {
+    const int lane = threadIdx.x & 63;
+    y = row;
+    if (P.slots == 1) {
+      if (y >= P.batch) return false;
+      b = y;
+      q = 0;
+      return true;
+    }
+    int64_t T = 0;
+    int mx = 0;
+    for (int c = 0; c < P.batch; c += 64) {
+      int l = 0;
+      if (c + lane < P.batch) {
+        const int L = seq_prefix_len(P, c + lane);
+        l = L - seq_lo(P, L) + P.draft;
+      }
+      int64_t sum = l;
+      int m = l;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        sum += __shfl_xor(sum, off, 64);
+        m = max(m, __shfl_xor(m, off, 64));
+      }
+      T += sum;
+      mx = max(mx, m);
+    }
+    T = uniform64(T);
+    mx = __builtin_amdgcn_readfirstlane(mx);
+    const int nwy = gridDim.y;
+    int64_t qq = (T + nwy - 1) / nwy;
+    const int64_t qs = ((int64_t)mx + P.slots - 2) / (P.slots - 1);
+    if (qs > qq) qq = qs;
+    if (qq < P.min_q) qq = P.min_q;
+    q = qq;
+    a = (int64_t)y * q;
+    if (a >= T) return false;
+    e = a + q < T ? a + q : T;
+    // the sequence holding key a: inclusive scan of len over 64 sequences at a time
+    int64_t base = 0;
+    for (int c = 0; c < P.batch; c += 64) {
+      int l = 0;
+      if (c + lane < P.batch) {
+        const int L = seq_prefix_len(P, c + lane);
+        l = L - seq_lo(P, L) + P.draft;
+      }
+      int64_t incl = l;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+      }
+      const uint64_t hit = __ballot(base + incl > a);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        b = c + f;
+        cum = uniform64(base + __shfl(incl, f, 64) - __shfl(l, f, 64));
+        return true;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    return false;  // unreachable for a < T
+  }
+
+  __device__ Piece piece(const FwdParams& P) {
+    Piece pc;
+    pc.b = b;
+    pc.L = seq_prefix_len(P, b);
+    const int lo = seq_lo(P, pc.L);
+    len = pc.L - lo + P.draft;
+    if (P.slots == 1) {
+      pc.t0 = lo;
+      pc.t1 = pc.L + P.draft;
+      pc.slot = 0;
+      pc.count = 1;
+      return pc;
+    }
+    const int64_t s0 = a > cum ? a : cum;
+    const int64_t s1 = e < cum + len ? e : cum + len;
+    pc.t0 = lo + (int)(s0 - cum);
+    pc.t1 = lo + (int)(s1 - cum);
+    const int64_t first = cum / q, last = (cum + len - 1) / q;
+    pc.slot = (int)(y - first);
+    pc.count = (y == last) ? (int)(last - first + 1) : 0;
+    return pc;
+  }
+
+  // Advances to the next sequence of the range; false at its end.
+  __device__ bool next(const FwdParams& P) {
+    if (P.slots == 1) return false;
+    cum += len;
+    if (cum >= e || b + 1 >= P.batch) return false;
+    ++b;
+    return true;
+  }
 };
 
 // Validates args (host only) and fills the plan.  Returns a VA_ status.  Pointer

@@ -33,21 +33,27 @@ int max_attended_prefix(int max_prefix_len, int window_left) {
                           : max_prefix_len;
 }
 
-int round_up(int x, int m) { return (x + m - 1) / m * m; }
+constexpr int kMaxSlots = 256;  // heuristic cap on partial slots per (sequence, KV head)
 
-// Split heuristic.  A split is one workgroup streaming `chunk` prefix tokens of its
-// KV heads; `per_cu` workgroups fit on a compute unit at once.  One full round of
-// workgroups across the chip (per_cu x CUs) measured best: each workgroup streams
-// long runs, and the fp32 partial it writes (rows x (v_dim+1) x 4 B per head) stays
-// small beside its KV bytes.  Chunks stay >= 128 tokens.
-int heuristic_splits(int batch, int head_groups, int max_leff, int cus, int per_cu) {
-  const long long units = (long long)batch * head_groups;
-  if (max_leff <= 0 || units <= 0) return 1;
-  const long long target = (long long)cus * per_cu;
-  long long s = (target + units - 1) / units;
-  const long long s_max = (max_leff + 127) / 128;
-  if (s > s_max) s = s_max;
-  return s < 1 ? 1 : (int)s;
+// Split heuristic: how many key ranges (grid rows) and partial slots.  The grid
+// is one full round of workgroups across the chip (per_cu x CUs, with head_groups
+// workgroups per range), and the device cuts the keys of all sequences into that
+// many equal ranges.  The slot count bounds the pieces of one sequence: about
+// twice its even share of the ranges, so the bound rarely limits the balance,
+// and never more than a sequence of the host's maximum length can need.
+void heuristic_grid(int batch, int head_groups, int maxlen, int min_q, int cus, int per_cu,
+                    int* nwy, int* slots) {
+  const long long rows = ((long long)cus * per_cu + head_groups - 1) / head_groups;
+  *nwy = (int)(rows < 1 ? 1 : (rows > 65535 ? 65535 : rows));
+  if (batch <= 0 || maxlen <= 0) {
+    *slots = 1;
+    return;
+  }
+  long long s = (2LL * *nwy + batch - 1) / batch + 1;
+  const long long s_need = (long long)(maxlen - 1) / min_q + 2;  // pieces of a maxlen sequence
+  if (s > s_need) s = s_need;
+  if (s > kMaxSlots) s = kMaxSlots;
+  *slots = (int)(s < 2 ? 2 : s);
 }
 
 }  // namespace
@@ -147,14 +153,21 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
     head_groups = (a->hkv + p->hpc - 1) / p->hpc;
     per_cu = (a->qk_dim == 128 && p->rt == 1) ? 2 : 1;
   }
+  p->hg = head_groups;
   p->lg_page = ilog2(a->page_size);
   p->max_leff = max_attended_prefix(a->max_prefix_len, a->window_left);
-  p->splits = a->num_splits > 0 ? a->num_splits
-                                 : heuristic_splits(a->batch, head_groups, p->max_leff,
-                                                    device_cu_count(), per_cu);
-  p->chunk = p->max_leff > 0 ? round_up((p->max_leff + p->splits - 1) / p->splits, kTokBlock)
-                             : kTokBlock;
-  p->ws_o_floats = (int64_t)a->batch * a->hkv * p->splits * rows * a->v_dim;
+  // fewest keys per workgroup: a few blocks of the kernel's main loop
+  p->min_q = p->kind == kMlaFp8 ? 128 : (p->kind == kTile ? 64 : 64);
+  const long long maxlen = (long long)p->max_leff + a->draft_len;
+  const int maxlen_i = maxlen > INT32_MAX ? INT32_MAX : (int)maxlen;
+  int nwy = 1, slots = 1;
+  heuristic_grid(a->batch, head_groups, maxlen_i, p->min_q, device_cu_count(), per_cu, &nwy, &slots);
+  p->slots = a->num_splits > 0 ? a->num_splits : slots;
+  // one slot: grid row y takes all of sequence y
+  p->nwy = p->slots == 1 ? (a->batch > 0 ? a->batch : 1) : nwy;
+  if (p->nwy > 65535) return VA_EUNSUPPORTED;
+  p->ws_o_floats = (int64_t)a->batch * a->hkv * p->slots * rows * a->v_dim;
+  p->ws_cnt_floats = p->ws_o_floats + (int64_t)a->batch * a->hkv * p->slots * rows;
   return VA_OK;
 }
 
@@ -180,7 +193,7 @@ int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int3
   if (batch < 0 || hkv < 1 || hq < 1 || hq % hkv || draft_len < 1 || v_dim < 1 || num_splits < 1)
     return -1;
   const int64_t rows = (int64_t)(hq / hkv) * draft_len;
-  return (int64_t)batch * hkv * num_splits * rows * ((int64_t)v_dim + 1) * 4;
+  return ((int64_t)batch * hkv * num_splits * rows * ((int64_t)v_dim + 1) + batch) * 4;
 }
 
 int32_t verify_attn_num_splits(const verify_attn_args* args) {
@@ -188,7 +201,7 @@ int32_t verify_attn_num_splits(const verify_attn_args* args) {
   if (!args) return -1;
   verify_attn_args a = *args;
   a.num_splits = 0;  // the heuristic's choice, whatever the caller asked for
-  return va::make_plan(&a, &p, /*check_pointers=*/false) == VA_OK ? p.splits : -1;
+  return va::make_plan(&a, &p, /*check_pointers=*/false) == VA_OK ? p.slots : -1;
 }
 
 int verify_attn_can_handle(const verify_attn_args* args) {
@@ -198,7 +211,7 @@ int verify_attn_can_handle(const verify_attn_args* args) {
 
 static int check_workspace(const verify_attn_args* a, const va::Plan& p) {
   const int64_t need = verify_attn_workspace_bytes(a->batch, a->hkv, a->hq, a->draft_len,
-                                                   a->v_dim, p.splits);
+                                                   a->v_dim, p.slots);
   return (need < 0 || a->workspace_bytes < need) ? VA_EWORKSPACE : VA_OK;
 }
 

@@ -112,7 +112,7 @@ def test_gate_rejects(kw, status):
 
 def test_workspace_checked_before_launch():
     need = B.verify_attn_workspace_bytes(2, 2, 8, 4, 128, 4)
-    assert need == 2 * 2 * 4 * 16 * 129 * 4
+    assert need == (2 * 2 * 4 * 16 * 129 + 2) * 4     # partials + one piece count per sequence
     assert fwd(workspace_bytes=need - 1) == B.VA_EWORKSPACE
     assert combine(workspace_bytes=need - 1) == B.VA_EWORKSPACE
 

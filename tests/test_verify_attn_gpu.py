@@ -112,6 +112,36 @@ def test_split_counts(splits):
     check(p, num_splits=splits)
 
 
+# The split-KV pass cuts the keys of all sequences, laid end to end, into equal
+# ranges; a range can end inside a sequence, span several short ones, or hold only
+# draft keys.  These mixes and slot counts push every case of that partition.
+MIXES = [
+    [0, 1, 5000, 3, 0, 700, 64, 2, 1500],   # one long sequence among short ones
+    [2500, 0, 0, 0],                         # one sequence holds almost every key
+    [0, 0, 0],                               # draft keys only
+]
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2])
+@pytest.mark.parametrize("mix", range(len(MIXES)))
+@pytest.mark.parametrize("splits", [0, 2, 5])
+def test_partition_length_mixes(dims, mix, splits):
+    lens = MIXES[mix]
+    p = W.make_problem(name="mix", batch=len(lens), prefix_lens=lens, hq=16 if dims == 2 else 8,
+                       hkv=1 if dims == 2 else 2, page_size=16, seed=300 + 10 * mix + dims,
+                       **DIMS[dims])
+    check(p, num_splits=splits)
+
+
+@pytest.mark.parametrize("window", [-1, 40])
+def test_partition_many_short_sequences(window):
+    # 300 sequences: one workgroup's range spans many of them
+    p = W.make_problem(name="many", batch=300, prefix_range=(0, 90), hq=4, hkv=1, qk_dim=128,
+                       page_size=4, window_left=window, seed=330 + max(window, 0))
+    check(p)
+    check(p, num_splits=1)
+
+
 @pytest.mark.parametrize("window", [0, 1, 3, 4, 17, 256, 5000])
 @pytest.mark.parametrize("dims", [0, 1, 2])
 def test_windows(window, dims):
