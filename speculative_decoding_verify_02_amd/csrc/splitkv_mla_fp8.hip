@@ -2,32 +2,37 @@
 // qk_dim = 576 e4m3fn bytes, with V the first v_dim = 512 bytes of the same row
 // (PR #23146 review: qk_head_dim differs from v_head_dim; V is read from the K
 // cache view).  The dense M dimension is G*D <= 64 query rows (16 heads x 4 drafts
-// on one GPU's share), so each token costs ~140 kflop: this kernel is built to keep
-// the MFMA pipes busy while streaming the cache.
+// on one GPU's share), so each key costs ~140 kflop: the kernel keeps the MFMA
+// pipes fed from LDS while the cache streams in behind them.
 //
-//   workgroup = (KV head g, key range y: pieces of sequences), 4 waves; wave w owns rows
-//   16w .. 16w+15.  Blocks of 128 tokens: the workgroup loads a block's K rows
-//   coalesced into registers (the next block's loads are in flight while the
-//   current block computes), stages them in one shared LDS tile, and every wave
-//   reads its operands from there.
+//   workgroup = (KV head g, key range y: pieces of sequences), 4 waves; wave w owns
+//   rows 16w .. 16w+15 and keeps their q in registers for the whole piece.
+//   Tiles of 128 keys stream into a two-tile LDS ring with global_load_lds_dwordx4
+//   (one wave instruction copies one key's 576-byte row, 36 lanes x 16 bytes), so
+//   no registers hold data in flight: the next tile lands while this one computes.
+//   Page ids travel the same way (global_load_lds_dword), so the vector-memory
+//   counter covers everything a wave waits for and one vmcnt(0) per tile suffices.
+//   LDS rows sit at 592 t + 32 (t / 16) bytes: the 16 rows of an MFMA operand read
+//   and the 8 rows of a transposed read all fall on distinct banks.
 //   QK: S^T = K Q^T.  For d < 512 with v_mfma_f32_16x16x128_f8f6f4: K bytes as
 //       they are, and the bf16 q as two e4m3 terms hi + lo/16 (the lo product is
 //       scaled by 2^-4 through the MFMA's MX block scale), ~2^-9 relative error in
 //       q, the precision bf16 itself carries.  The rope tail d in [512, 576) uses
 //       v_mfma_f32_16x16x32_bf16 with K widened exactly to bf16 (every e4m3fn value
 //       is a bf16 value) and q in bf16.
-//   softmax: online, exp2 domain, row max across the 4 lanes of a row.
+//   softmax: online, exp2 domain, row max across the 4 lanes of a row.  The
+//       reference max moves only when a score passes it by more than one (log2
+//       units), so p <= 2 and most tiles skip rescaling the accumulator.
 //   PV: O^T += V^T P^T with v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3).  P enters
-//       as two e4m3 terms, hi = e4m3(256 p) and lo = e4m3(16 (256 p - hi)) with the
+//       as two e4m3 terms, hi = e4m3(128 p) and lo = e4m3(16 (128 p - hi)) with the
 //       lo product scaled by 2^-4 through the MFMA's MX block scale: about 8
-//       significant bits per probability, close to bf16.  p <= 1, so 256 p never
-//       overflows, and the factor keeps small probabilities out of the subnormal
-//       range; it is divided out at the end.  The running sum l uses the
-//       unrounded fp32 p.  The A operand (32 tokens
-//       of one V column per lane) comes from four ds_read_b64_tr_b8 transposed LDS
-//       reads: in each 16-lane group, lanes 2k and 2k+1 address the two 8-byte
-//       halves of a 16-column slice of token row k, and lane c receives column c of
-//       the 8 rows.
+//       significant bits per probability, close to bf16.  128 p <= 256 never
+//       overflows e4m3, and the factor keeps small probabilities out of the
+//       subnormal range; it is divided out at the end.  The running sum l uses the
+//       unrounded fp32 p.  The A operand (32 keys of one V column per lane) comes
+//       from four ds_read_b64_tr_b8 transposed LDS reads: in each 16-lane group,
+//       lanes 2k and 2k+1 address the two 8-byte halves of a 16-column slice of key
+//       row k, and lane c receives column c of the 8 rows.
 
 #include <limits.h>
 #include <math.h>
@@ -38,15 +43,15 @@ namespace va {
 
 namespace {
 
-constexpr int kMB = 128;              // tokens per block
+constexpr int kMB = 128;              // keys per tile
 constexpr int kKRB = 576;             // K row bytes
 constexpr int kVRB = 512;             // V bytes per row (first part of the K row)
-constexpr int kRS = kKRB + 16;        // LDS row stride: 16-lane operand reads hit distinct banks
-constexpr int kNCH = kKRB / 16;       // 16-byte chunks per row
-constexpr int kNLD = kMB * kNCH / 256;  // coalesced loads per thread per block
+constexpr int kRS = kKRB + 16;        // LDS row stride
+constexpr int kTileBytes = 76032;     // row_off(127) + 576, rounded up to 128
 constexpr int kCT = kVRB / 16;        // O^T column tiles
-constexpr int kQRS = 2 * kKRB + 16;  // LDS row stride of a wave's bf16 Q rows
-constexpr float kPScale = 256.f;
+constexpr int kKPW = kMB / kWaves;    // keys each wave copies per tile
+constexpr float kPScale = 128.f;      // P scale for e4m3 (p <= 2^kLazy, so 128 p <= 256 < 448)
+constexpr float kLazy = 1.f;          // log2 headroom before the running max is moved
 constexpr int kE8M0One = 127;         // MX block scale exponents (bias 127)
 constexpr int kE8M0Sixteenth = 123;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -56,6 +61,12 @@ typedef __attribute__((__vector_size__(8 * sizeof(uint32_t)))) uint32_t u32x8;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// Byte offset of key row t inside a tile.  The 16-byte slot of row t mod 16 is
+// 5 t + 2 (t / 16): distinct for the 16 consecutive rows of an operand read and for
+// the rows {4j + i, 16 + 4j + i} (i < 4) a transposed read takes together.
+__device__ __forceinline__ int row_off(int t) { return t * kRS + (t >> 4) * 32; }
+static_assert(127 * kRS + 7 * 32 + kKRB <= kTileBytes, "tile holds 128 rows");
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -69,210 +80,248 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t x) {
   return r;
 }
 
-// Slots of the block's tokens t0 + lane and t0 + 64 + lane (clamped to the piece).
-__device__ __forceinline__ void block_slots(const int32_t* bt_row, int t0, int t_last, int lane,
-                                            int lg, int pmask, int& sa, int& sb) {
-  const int ta = min(t0 + lane, t_last), tb = min(t0 + 64 + lane, t_last);
-  sa = (bt_row[ta >> lg] << lg) | (ta & pmask);
-  sb = (bt_row[tb >> lg] << lg) | (tb & pmask);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+
+// Copies to LDS at `lds` + lane * size straight from global memory.  Inline assembly,
+// so the compiler (which does not see these copies) adds no waits of its own before
+// LDS reads; the waits are explicit.  M0 holds the wave's LDS base and needs one
+// wait state before the copy reads it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Token of score slot i (0..31) of lane group j: tile i/4, accumulator row 4j + i%4.
 __device__ __forceinline__ int slot_token(int j, int i) { return 16 * (i >> 2) + 4 * j + (i & 3); }
 
-// LDS of the one workgroup a compute unit holds: the shared K tile and each wave's
-// staged Q rows.
-__shared__ __attribute__((aligned(16))) uint8_t s_tile[kMB * kRS];
-__shared__ __attribute__((aligned(16))) uint8_t s_qtile[kWaves][16 * kQRS];
+// LDS of the one workgroup a compute unit holds: the two-tile ring and each wave's
+// page ids for its keys of the next two tiles.
+__shared__ __attribute__((aligned(128))) uint8_t s_ring[2][kTileBytes];
+__shared__ __attribute__((aligned(16))) int32_t s_pid[2][kWaves][kKPW];
 
-// One piece: keys [pc.t0, pc.t1) of sequence pc.b for KV head g -> partial slot
-// pc.slot.  Kept out of line so the piece loop adds no register pressure to it.
-__device__ __noinline__ void mla_piece(const FwdParams& P, const Piece pc, int g) {
-  uint8_t* tile = s_tile;
+}  // namespace
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void splitkv_mla_fp8_kernel(FwdParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int j = lane >> 4;
+  const int g = blockIdx.x;
+  PieceWalk pw;
+  if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
+
   const int row = wave * 16 + n;
   const bool rv = row < P.rows;
   const int row_i = rv ? row / P.group : 0;  // draft index of this lane's row
-  uint8_t* qw = s_qtile[wave];
   const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
+
+  do {
+  const Piece pc = pw.piece(P);
   const int b = pc.b;
   const int L = pc.L;
   const int t_begin = pc.t0, t_end = pc.t1;
-  const int nblk = (t_end - t_begin + kMB - 1) / kMB;
+  const int ntile = (t_end - t_begin + kMB - 1) / kMB;
   const int t_last = t_end - 1;
   if (pc.count > 0 && g == 0 && tid == 0) P.counts[b] = pc.count;
+  const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
 
-  // this wave's 16 Q rows go to its own LDS rows: for d < 512 as two e4m3 terms
-  // (hi = e4m3(q), lo = e4m3(16 (q - hi)), together ~2^-9 relative error, the
-  // precision of the bf16 q itself) for the fp8 MFMA, and the 64-wide rope tail
-  // d >= 512 as bf16.  Row layout: hi[512] | lo[512] | bf16 tail[64].
+  // page ids of this wave's keys of tile k -> s_pid[k % 2][wave]: entry e is the
+  // page of the wave's first key plus e, clamped to the table row
+  auto copy_pids = [&](int k) {
+    const int tw = min(t_begin + k * kMB + wave * kKPW, t_last);
+    const int e = min((tw >> lg) + lane, P.max_pages - 1);
+    if (lane < kKPW) dma4(bt_row + e, lds_addr(&s_pid[k & 1][wave][0]));
+  };
+  // this wave's keys of tile k -> ring buffer k % 2 (one key row per instruction).
+  // Lane l < 32 looks up the slot of key l with one LDS read; each copy then takes
+  // its key's row offset from that lane.
+  auto copy_tile = [&](int k) {
+    const int t0 = t_begin + k * kMB + wave * kKPW;
+    const int pbase = min(t0, t_last) >> lg;
+    uint8_t* ring = s_ring[k & 1];
+    const int tl = min(t0 + (lane & (kKPW - 1)), t_last);
+    const int page = s_pid[k & 1][wave][(tl >> lg) - pbase];
+    const int64_t off = (((int64_t)page << lg) | (tl & pmask)) * P.k_sslot;
+    const uint32_t off_lo = (uint32_t)off, off_hi = (uint32_t)((uint64_t)off >> 32);
+#pragma unroll
+    for (int u = 0; u < kKPW; ++u) {
+      const uint64_t ou = ((uint64_t)__builtin_amdgcn_readlane(off_hi, u) << 32) |
+                          __builtin_amdgcn_readlane(off_lo, u);
+      if (lane < kKRB / 16) dma16(kg + ou + 16 * lane, lds_addr(ring + row_off(wave * kKPW + u)));
+    }
+  };
+
+  copy_pids(0);
+  if (ntile > 1) copy_pids(1);
+  wait_copies();
+  copy_tile(0);
+
+  // this wave's 16 q rows in registers: for d < 512 as two e4m3 terms (hi = e4m3(q),
+  // lo = e4m3(16 (q - hi)), together ~2^-9 relative error, the precision of the
+  // bf16 q itself), the 64-wide rope tail d >= 512 as bf16.  Lane group j holds
+  // elements 128kb + 32j + [0, 32) (and 512 + 32h + 8j + [0, 8) of the tail), the
+  // k-slots of the K operand read below.
+  i32x8 qh[kVRB / 128], ql[kVRB / 128];
+  u32x4 qr[2];
   {
+    const int hh = rv ? row % P.group : 0;
+    const uint8_t* qp =
+        P.q + (int64_t)(b * P.draft + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
-    for (int c = 0; c < 16 * (kVRB / 8) / 64; ++c) {       // 16 chunks of 8 values per lane
-      const int q = 64 * c + lane;
-      const int r = q / (kVRB / 8), ch = q % (kVRB / 8);
-      const int qrow = wave * 16 + r;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qrow < P.rows) {
-        const int i = qrow / P.group, hh = qrow % P.group;
-        raw = *reinterpret_cast<const u32x4*>(P.q + (int64_t)(b * P.draft + i) * P.q_srow +
-                                              (int64_t)(g * P.group + hh) * P.q_shead + 16 * ch);
-      }
-      float x[8];  // q elements, saturated to the e4m3 range (+-448)
+    for (int kb = 0; kb < kVRB / 128; ++kb) {
+      u32x4 raw[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = fminf(fmaxf(__uint_as_float(raw[e] << 16), -448.f), 448.f);
-        x[2 * e + 1] = fminf(fmaxf(__uint_as_float(raw[e] & 0xffff0000u), -448.f), 448.f);
-      }
-      uint32_t hi[2], lo[2];
+      for (int c = 0; c < 4; ++c)
+        raw[c] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (128 * kb + 32 * j + 8 * c))
+                    : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h], x[4 * h + 1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2], x[4 * h + 3], w, true);
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        int wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h] - a[0]) * 16.f,
-                                                 (x[4 * h + 1] - a[1]) * 16.f, 0, false);
-        wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h + 2] - c2[0]) * 16.f,
-                                             (x[4 * h + 3] - c2[1]) * 16.f, wl, true);
-        hi[h] = (uint32_t)w;
-        lo[h] = (uint32_t)wl;
+      for (int c = 0; c < 4; ++c) {
+        float x[8];  // q elements, saturated to the e4m3 range (+-448)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = fminf(fmaxf(__uint_as_float(raw[c][e] << 16), -448.f), 448.f);
+          x[2 * e + 1] = fminf(fmaxf(__uint_as_float(raw[c][e] & 0xffff0000u), -448.f), 448.f);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h], x[4 * h + 1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2], x[4 * h + 3], w, true);
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+          const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+          int wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h] - a[0]) * 16.f,
+                                                   (x[4 * h + 1] - a[1]) * 16.f, 0, false);
+          wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h + 2] - c2[0]) * 16.f,
+                                               (x[4 * h + 3] - c2[1]) * 16.f, wl, true);
+          qh[kb][2 * c + h] = w;
+          ql[kb][2 * c + h] = wl;
+        }
       }
-      *reinterpret_cast<u32x2*>(qw + r * kQRS + 8 * ch) = u32x2{hi[0], hi[1]};
-      *reinterpret_cast<u32x2*>(qw + r * kQRS + kVRB + 8 * ch) = u32x2{lo[0], lo[1]};
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {                             // 16 rows x 8 tail chunks
-      const int q = 64 * c + lane;
-      const int r = q / 8, ch = q % 8;
-      const int qrow = wave * 16 + r;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qrow < P.rows) {
-        const int i = qrow / P.group, hh = qrow % P.group;
-        raw = *reinterpret_cast<const u32x4*>(P.q + (int64_t)(b * P.draft + i) * P.q_srow +
-                                              (int64_t)(g * P.group + hh) * P.q_shead +
-                                              2 * kVRB + 16 * ch);
-      }
-      *reinterpret_cast<u32x4*>(qw + r * kQRS + 2 * kVRB + 16 * ch) = raw;
-    }
+    for (int h = 0; h < 2; ++h)
+      qr[h] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (kVRB + 32 * h + 8 * j))
+                 : u32x4{0u, 0u, 0u, 0u};
   }
   // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
   const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
   const int row_hi = rv ? min(t_last, L + row_i) : -1;
+  // keys every row of the wave sees: tiles inside [wave_lo, wave_hi] need no masking
+  int wave_lo = rv ? row_lo : INT_MIN, wave_hi = rv ? row_hi : INT_MAX;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    wave_lo = max(wave_lo, __shfl_xor(wave_lo, off, 64));
+    wave_hi = min(wave_hi, __shfl_xor(wave_hi, off, 64));
+  }
+  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[kCT];
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-
-  // coalesced block load: thread chunk q = 256u + tid -> token q / 36, chunk q % 36
-  u32x4 kreg[kNLD];
-  auto load = [&](int sa, int sb) {
-#pragma unroll
-    for (int u = 0; u < kNLD; ++u) {
-      const int q = 256 * u + tid;
-      const int tok = q / kNCH;
-      const int xa = __shfl(sa, tok & 63, 64), xb = __shfl(sb, tok & 63, 64);
-      const int sl = tok < 64 ? xa : xb;
-      kreg[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)sl * P.k_sslot + 16 * (q % kNCH));
-    }
-  };
-  int sa, sb, na = 0, nb = 0;
-  block_slots(bt_row, t_begin, t_last, lane, lg, pmask, sa, sb);
-  load(sa, sb);
-  if (nblk > 1) block_slots(bt_row, t_begin + kMB, t_last, lane, lg, pmask, na, nb);
-
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int t0 = t_begin + blk * kMB;
-    __syncthreads();  // every wave is done reading the previous block's tile
-#pragma unroll
-    for (int u = 0; u < kNLD; ++u) {
-      const int q = 256 * u + tid;
-      *reinterpret_cast<u32x4*>(tile + (q / kNCH) * kRS + 16 * (q % kNCH)) = kreg[u];
-    }
+  for (int k = 0; k < ntile; ++k) {
+    // this wave's copies of tile k (and page ids of tile k + 1) have landed; the
+    // barrier shows every wave's and frees the buffer tile k - 1 was computed from
+    wait_copies();
     __syncthreads();
-    if (blk + 1 < nblk) {
-      load(na, nb);  // next block in flight during this block's math
-      if (blk + 2 < nblk) block_slots(bt_row, t0 + 2 * kMB, t_last, lane, lg, pmask, na, nb);
-    }
+    if (k + 1 < ntile) copy_tile(k + 1);
+    if (k + 2 < ntile) copy_pids(k + 2);
+
+    const int t0 = t_begin + k * kMB;
+    const uint8_t* tile = s_ring[k & 1];
 
     // a4: S^T for 8 token tiles
     f32x4 sacc[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // d < 512: fp8 x fp8 (K bytes as they are, q as hi + lo terms); lane group j
-    // holds elements 128kb + 32j + [0, 32) of its token (A) and of its row (B)
+    // d < 512: fp8 x fp8 (K bytes as they are, q as hi + lo terms).  Token tiles go
+    // in pairs so the two products into one accumulator are not back to back.
 #pragma unroll
     for (int kb = 0; kb < kVRB / 128; ++kb) {
-      const uint8_t* qp = qw + n * kQRS + 128 * kb + 32 * j;
-      const u32x4 h0 = *reinterpret_cast<const u32x4*>(qp);
-      const u32x4 h1 = *reinterpret_cast<const u32x4*>(qp + 16);
-      const u32x4 l0 = *reinterpret_cast<const u32x4*>(qp + kVRB);
-      const u32x4 l1 = *reinterpret_cast<const u32x4*>(qp + kVRB + 16);
-      const i32x8 qh = __builtin_bit_cast(i32x8, u32x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]});
-      const i32x8 ql = __builtin_bit_cast(i32x8, u32x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]});
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const uint8_t* kp = tile + (16 * tt + n) * kRS + 128 * kb + 32 * j;
-        const u32x4 k0 = *reinterpret_cast<const u32x4*>(kp);
-        const u32x4 k1 = *reinterpret_cast<const u32x4*>(kp + 16);
-        const i32x8 ka = __builtin_bit_cast(i32x8, u32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
-        sacc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh, sacc[tt], 0, 0, 0, 0, 0, 0);
-        sacc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql, sacc[tt], 0, 0, 0,
-                                                                    kE8M0One, 0, kE8M0Sixteenth);
+      for (int tt = 0; tt < 8; tt += 2) {
+        i32x8 ka[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint8_t* kp = tile + row_off(16 * (tt + e) + n) + 128 * kb + 32 * j;
+          const u32x4 k0 = *reinterpret_cast<const u32x4*>(kp);
+          const u32x4 k1 = *reinterpret_cast<const u32x4*>(kp + 16);
+          ka[e] = __builtin_bit_cast(i32x8, u32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], qh[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], ql[kb], sacc[tt + e], 0, 0, 0,
+                                                                          kE8M0One, 0, kE8M0Sixteenth);
       }
     }
     // rope tail d in [512, 576): bf16 k-steps, lane group j holds 512 + 32h + 8j + [0, 8)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const u32x4 qr = *reinterpret_cast<const u32x4*>(qw + n * kQRS + 2 * kVRB + 2 * (32 * h + 8 * j));
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const u32x2 kr = *reinterpret_cast<const u32x2*>(tile + (16 * tt + n) * kRS + kVRB + 32 * h + 8 * j);
+        const u32x2 kr = *reinterpret_cast<const u32x2*>(tile + row_off(16 * tt + n) + kVRB + 32 * h + 8 * j);
         const u32x2 w0 = fp8x4_to_bf16x4(kr[0]), w1 = fp8x4_to_bf16x4(kr[1]);
         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]}), as_bf16x8(qr), sacc[tt], 0, 0, 0);
+            as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]}), as_bf16x8(qr[h]), sacc[tt], 0, 0, 0);
       }
     }
 
     // online softmax over the lane's 32 scores (row n)
     float sc[32];
     float bmax = -INFINITY;
+    if (t0 >= wave_lo && t0 + kMB - 1 <= wave_hi) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int t = t0 + slot_token(j, e);
-      const bool ok = (t >= row_lo) && (t <= row_hi);
-      const float v = ok ? sacc[e >> 2][e & 3] * P.c_log2 : -INFINITY;
-      sc[e] = v;
-      bmax = fmaxf(bmax, v);
+      for (int e = 0; e < 32; ++e) {
+        sc[e] = sacc[e >> 2][e & 3] * P.c_log2;
+        bmax = fmaxf(bmax, sc[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int t = t0 + slot_token(j, e);
+        const bool ok = (t >= row_lo) && (t <= row_hi);
+        sc[e] = ok ? sacc[e >> 2][e & 3] * P.c_log2 : -INFINITY;
+        bmax = fmaxf(bmax, sc[e]);
+      }
     }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m_run, bmax);
+    // the reference max moves only when a score passes it by more than kLazy, so
+    // most tiles leave the accumulator alone; p = 2^(s - m) stays <= 2^kLazy
+    const bool grow = bmax > m_run + kLazy;
+    const float m_new = grow ? bmax : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
       psum += sc[e];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // the accumulator lives in AGPRs: rescale only when some row's max moved
-    if (__any(alpha != 1.f)) {
+    // the accumulator lives in AGPRs: rescale only when some row with a nonzero
+    // accumulator moved its max
+    if (__any(grow && m_run != -INFINITY)) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) oacc[ct] *= alpha;
     }
-    // P in two e4m3 terms: hi = e4m3(256 p), lo = e4m3(16 (256 p - hi)); the lo
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // P in two e4m3 terms: hi = e4m3(128 p), lo = e4m3(16 (128 p - hi)); the lo
     // product enters the same accumulator through the MFMA's B scale 2^-4.  The
     // pair keeps about 8 significant bits of each probability.
     i32x8 pb, pl;
@@ -294,20 +343,27 @@ __device__ __noinline__ void mla_piece(const FwdParams& P, const Piece pc, int g
     __attribute__((address_space(3))) char* lbase = (__attribute__((address_space(3))) char*)tile;
     int voff[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) voff[r] = slot_token(j, 8 * r + (n >> 1)) * kRS + 8 * (n & 1);
+    for (int r = 0; r < 4; ++r) voff[r] = row_off(slot_token(j, 8 * r + (n >> 1))) + 8 * (n & 1);
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
-      i32x8 a;
+    for (int ct = 0; ct < kCT; ct += 2) {
+      i32x8 a[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            reinterpret_cast<lds_i32x2*>(lbase + voff[r] + 16 * ct));
-        a[2 * r] = x[0];
-        a[2 * r + 1] = x[1];
+      for (int e = 0; e < 2; ++e) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              reinterpret_cast<lds_i32x2*>(lbase + voff[r] + 16 * (ct + e)));
+          a[e][2 * r] = x[0];
+          a[e][2 * r + 1] = x[1];
+        }
       }
-      oacc[ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pb, oacc[ct], 0, 0, 0, 0, 0, 0);
-      oacc[ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pl, oacc[ct], 0, 0, 0, kE8M0One,
-                                                                  0, kE8M0Sixteenth);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pb, oacc[ct + e], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pl, oacc[ct + e], 0, 0, 0,
+                                                                        kE8M0One, 0, kE8M0Sixteenth);
     }
   }
 
@@ -328,16 +384,7 @@ __device__ __noinline__ void mla_piece(const FwdParams& P, const Piece pc, int g
     if (j == 0)
       P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
-}
-
-}  // namespace
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-void splitkv_mla_fp8_kernel(FwdParams P) {
-  PieceWalk pw;
-  if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
-  do {
-    mla_piece(P, pw.piece(P), blockIdx.x);
+  __syncthreads();  // every wave is done with the ring before the next piece refills it
   } while (pw.next(P));
 }
 

@@ -85,8 +85,14 @@ struct Piece {
   int count;   // on the sequence's last piece, its number of pieces; else 0
 };
 
+// Read-only int32 tables (prefix lengths, block table) through the constant address
+// space: a wave-uniform index then becomes a scalar load.
+__device__ __forceinline__ int load_ro(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 __device__ __forceinline__ int seq_prefix_len(const FwdParams& P, int b) {
-  return max(P.prefix_lens[b], 0);
+  return max(load_ro(P.prefix_lens, b), 0);
 }
 
 __device__ __forceinline__ int seq_lo(const FwdParams& P, int L) {
@@ -170,8 +176,8 @@ struct PieceWalk {
 
   __device__ Piece piece(const FwdParams& P) {
     Piece pc;
-    pc.b = b;
-    pc.L = seq_prefix_len(P, b);
+    pc.b = __builtin_amdgcn_readfirstlane(b);
+    pc.L = __builtin_amdgcn_readfirstlane(seq_prefix_len(P, pc.b));
     const int lo = seq_lo(P, pc.L);
     len = pc.L - lo + P.draft;
     if (P.slots == 1) {
@@ -188,6 +194,10 @@ struct PieceWalk {
     const int64_t first = cum / q, last = (cum + len - 1) / q;
     pc.slot = (int)(y - first);
     pc.count = (y == last) ? (int)(last - first + 1) : 0;
+    pc.t0 = __builtin_amdgcn_readfirstlane(pc.t0);
+    pc.t1 = __builtin_amdgcn_readfirstlane(pc.t1);
+    pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
+    pc.count = __builtin_amdgcn_readfirstlane(pc.count);
     return pc;
   }
 
