@@ -13,9 +13,11 @@ from .verify_attn_oracle import (  # noqa: F401
     decode_kv,
     e4m3fn_to_f64,
     lse_merge,
+    problem_fields,
     run,
     run_block_table,
     run_split,
+    translate_slots,
     verify_attention,
     verify_attention_split,
     visible_keys,

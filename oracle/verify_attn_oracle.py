@@ -35,6 +35,24 @@ Readings taken where the pages are silent (each is listed with its status):
   6. fp8 is OCP e4m3fn; the dequantised value is code * scale.
   7. MLA: V is the first v_dim columns of the K row.
   8. Block-table padding is page id 0 (parity unpinned by the pages: convention).
+
+Extensions beyond topk = 1 (the split-KV page lists them as what its fast path
+leaves to the fallback: sinks, logit cap, ragged extend; the overlap-spec page
+covers draft-extend with ``cu_seqlens_q`` from ``accept_length``; the page-size
+page leaves topk > 1 to a later change; the unified-attention page translates
+full-pool slots to a sliding-window pool):
+  9. Ragged rows (draft-extend): sequence b owns the query rows
+     qo_indptr[b] .. qo_indptr[b+1]-1, n_b of them, the last n_b tokens of its KV
+     (positions L_b .. L_b + n_b - 1); row i sees keys t <= L_b + i as above.
+ 10. Tree verify (topk > 1): the prefix is paged as before, but draft key j of
+     sequence b lives at an arbitrary slot draft_slots[b, j], and row i sees draft
+     key j iff tree_mask[b, i, j] is set (instead of j <= i).  No window.
+ 11. Attention sinks: one extra logit sinks[h] per q head joins the softmax
+     denominator with a zero value vector (so LSE includes it).
+ 12. Logit cap: scaled scores s become cap * tanh(s / cap) before the softmax
+     (cap > 0; sinks are not capped).
+ 13. Sliding-window pool: full-pool slot s maps to full_to_swa[s] in the window
+     pool; the window pool's block table is built from the mapped slots.
 """
 
 from __future__ import annotations
@@ -125,48 +143,80 @@ def _sequence_kv(b, kv_indptr, kv_indices, k_cache, v_cache, qk_dim, v_dim, kv_d
     return K, V
 
 
-def attend(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
-    """softmax(sm_scale * K q) V and the natural-log LSE, for one query row (fp64)."""
-    if K.shape[0] == 0:
+def attend(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
+           logit_cap: float = 0.0, sink: Optional[float] = None):
+    """softmax(s) V and the natural-log LSE for one query row (fp64), s = sm_scale * K q.
+
+    With ``logit_cap`` > 0 the scores are s -> cap * tanh(s / cap) first (reading 12);
+    a ``sink`` logit joins the denominator with a zero value vector (reading 11)."""
+    s = sm_scale * (K @ q_row) if K.shape[0] else np.zeros(0)
+    if logit_cap > 0:
+        s = logit_cap * np.tanh(s / logit_cap)
+    allx = s if sink is None else np.append(s, float(sink))
+    if allx.size == 0 or np.all(allx == -math.inf):
         return np.zeros(V.shape[1]), -math.inf
-    s = sm_scale * (K @ q_row)
-    m = s.max()
+    m = allx.max()
     w = np.exp(s - m)
-    z = w.sum()
+    z = np.exp(allx - m).sum()
     return (w @ V) / z, m + math.log(z)
+
+
+def translate_slots(kv_indices: np.ndarray, full_to_swa: np.ndarray) -> np.ndarray:
+    """Full-pool slots -> sliding-window-pool slots through the pool's map (reading 13)."""
+    return np.asarray(full_to_swa, dtype=np.int64)[np.asarray(kv_indices, dtype=np.int64)]
 
 
 def verify_attention(q, k_cache, v_cache, kv_indptr, kv_indices, prefix_lens, draft_len,
                      hq, hkv, qk_dim, v_dim, sm_scale, window_left=-1, kv_dtype=0,
-                     k_scale=1.0, v_scale=1.0, rows: Optional[Sequence[int]] = None):
-    """The verify output O [B*D, Hq, v_dim] and LSE [B*D, Hq], in float64.
+                     k_scale=1.0, v_scale=1.0, rows: Optional[Sequence[int]] = None,
+                     qo_indptr=None, draft_slots=None, tree_mask=None, sinks=None,
+                     logit_cap: float = 0.0):
+    """The verify output O [rows, Hq, v_dim] and LSE [rows, Hq], in float64.
 
-    ``q`` holds bf16 bits [B*D, Hq, qk_dim]; the caches hold raw elements
-    [num_slots, Hkv, row]; ``v_cache`` may be ``k_cache`` itself when V is the
-    first v_dim columns of the K row.  ``rows`` optionally restricts the work to
-    the given query rows (others stay NaN) so large problems can be sampled.
+    ``q`` holds bf16 bits [rows, Hq, qk_dim] (rows = B*D, or qo_indptr[B] with
+    ragged rows); the caches hold raw elements [num_slots, Hkv, row]; ``v_cache``
+    may be ``k_cache`` itself when V is the first v_dim columns of the K row.
+    ``rows`` optionally restricts the work to the given query rows (others stay
+    NaN) so large problems can be sampled.  ``qo_indptr``, ``draft_slots`` with
+    ``tree_mask``, ``sinks`` and ``logit_cap`` select readings 9-12.
     """
     B = len(prefix_lens)
     G = hq // hkv
-    O = np.full((B * draft_len, hq, v_dim), np.nan)
-    LSE = np.full((B * draft_len, hq), np.nan)
+    tree = draft_slots is not None
+    if qo_indptr is None:
+        qo = np.arange(B + 1, dtype=np.int64) * draft_len
+    else:
+        qo = np.asarray(qo_indptr, dtype=np.int64)
+    R = int(qo[B])
+    O = np.full((R, hq, v_dim), np.nan)
+    LSE = np.full((R, hq), np.nan)
     wanted = None if rows is None else set(int(r) for r in rows)
     for b in range(B):
-        rows_b = [b * draft_len + i for i in range(draft_len)]
+        rows_b = list(range(int(qo[b]), int(qo[b + 1])))
         if wanted is not None and not wanted.intersection(rows_b):
             continue
         K, V = _sequence_kv(b, kv_indptr, kv_indices, k_cache, v_cache, qk_dim, v_dim,
                             kv_dtype, k_scale, v_scale)
         L = int(prefix_lens[b])
-        for i in range(draft_len):
-            r = b * draft_len + i
+        if tree:
+            ds = np.asarray(draft_slots[b], dtype=np.int64)
+            Kd = decode_kv(k_cache[ds, :, :qk_dim], kv_dtype) * k_scale
+            Vd = decode_kv(v_cache[ds, :, :v_dim], kv_dtype) * v_scale
+        for i, r in enumerate(rows_b):
             if wanted is not None and r not in wanted:
                 continue
-            vis = visible_keys(L, i, window_left)
+            if tree:
+                sel = np.nonzero(np.asarray(tree_mask[b, i]) != 0)[0]
+                Kr = np.concatenate([K[:L], Kd[sel]], axis=0)
+                Vr = np.concatenate([V[:L], Vd[sel]], axis=0)
+            else:
+                vis = visible_keys(L, i, window_left)
+                Kr, Vr = K[vis], V[vis]
             for h in range(hq):
                 g = h // G
                 qf = bf16_to_f64(q[r, h, :qk_dim])
-                O[r, h], LSE[r, h] = attend(qf, K[vis, g], V[vis, g], sm_scale)
+                sink = None if sinks is None else float(sinks[h])
+                O[r, h], LSE[r, h] = attend(qf, Kr[:, g], Vr[:, g], sm_scale, logit_cap, sink)
     return O, LSE
 
 
@@ -224,7 +274,8 @@ def verify_attention_split(q, k_cache, v_cache, kv_indptr, kv_indices, prefix_le
 # convenience wrappers taking an object with the input fields
 # ---------------------------------------------------------------------------
 
-def _fields(p):
+def problem_fields(p):
+    """verify_attention's base keyword arguments from an object carrying the inputs."""
     v_cache = p.k_cache if p.v_cache is None else p.v_cache
     return dict(q=p.q, k_cache=p.k_cache, v_cache=v_cache, kv_indptr=p.kv_indptr,
                 kv_indices=p.kv_indices, prefix_lens=p.prefix_lens, draft_len=p.draft_len,
@@ -233,13 +284,20 @@ def _fields(p):
                 v_scale=p.v_scale)
 
 
+def _ext_fields(p):
+    return dict(qo_indptr=getattr(p, "qo_indptr", None),
+                draft_slots=getattr(p, "draft_slots", None),
+                tree_mask=getattr(p, "tree_mask", None), sinks=getattr(p, "sinks", None),
+                logit_cap=float(getattr(p, "logit_cap", 0.0) or 0.0))
+
+
 def run(p, rows=None):
     """verify_attention on an object carrying the input arrays and scalars."""
-    return verify_attention(**_fields(p), rows=rows)
+    return verify_attention(**problem_fields(p), **_ext_fields(p), rows=rows)
 
 
 def run_split(p, num_splits):
-    return verify_attention_split(**_fields(p), num_splits=num_splits)
+    return verify_attention_split(**problem_fields(p), num_splits=num_splits)
 
 
 def run_block_table(p, max_pages=None):

@@ -92,6 +92,11 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds) : "memory", "m0");
 }
+// Same with a wave-uniform base in SGPRs and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(src), "s"(lds) : "memory", "m0");
@@ -145,20 +150,18 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   };
   // this wave's keys of tile k -> ring buffer k % 2 (one key row per instruction).
   // Lane l < 32 looks up the slot of key l with one LDS read; each copy then takes
-  // its key's row offset from that lane.
+  // its key's slot from that lane into a scalar base address.
   auto copy_tile = [&](int k) {
     const int t0 = t_begin + k * kMB + wave * kKPW;
     const int pbase = min(t0, t_last) >> lg;
     uint8_t* ring = s_ring[k & 1];
     const int tl = min(t0 + (lane & (kKPW - 1)), t_last);
-    const int page = s_pid[k & 1][wave][(tl >> lg) - pbase];
-    const int64_t off = (((int64_t)page << lg) | (tl & pmask)) * P.k_sslot;
-    const uint32_t off_lo = (uint32_t)off, off_hi = (uint32_t)((uint64_t)off >> 32);
+    const int slot_l = (s_pid[k & 1][wave][(tl >> lg) - pbase] << lg) | (tl & pmask);
 #pragma unroll
     for (int u = 0; u < kKPW; ++u) {
-      const uint64_t ou = ((uint64_t)__builtin_amdgcn_readlane(off_hi, u) << 32) |
-                          __builtin_amdgcn_readlane(off_lo, u);
-      if (lane < kKRB / 16) dma16(kg + ou + 16 * lane, lds_addr(ring + row_off(wave * kKPW + u)));
+      const int slot = __builtin_amdgcn_readlane(slot_l, u);
+      if (lane < kKRB / 16)
+        dma16_s(kg + (int64_t)slot * P.k_sslot, 16 * lane, lds_addr(ring + row_off(wave * kKPW + u)));
     }
   };
 

@@ -70,10 +70,21 @@ class Problem:
     kv_indices: np.ndarray        # int32 [sum n_b]
     page_ids: list                # per sequence: int64 array of its page ids (in order)
     num_pages: int                # pool size in pages
-    q: np.ndarray                 # uint16 [B*D, Hq, qk_dim]
+    q: np.ndarray                 # uint16 [rows, Hq, qk_dim]
     k_cache: np.ndarray           # uint16 / uint8 [num_slots, Hkv, k_row]
     v_cache: Optional[np.ndarray]  # same dtype [num_slots, Hkv, v_dim] or None (alias of K)
     seed: int = 0
+    # optional extensions (None / 0 = target verify at topk = 1)
+    qo_indptr: Optional[np.ndarray] = None    # int32 [B+1]: ragged draft rows per sequence
+    draft_slots: Optional[np.ndarray] = None  # int32 [B, D]: tree verify, slot of draft key j
+    tree_mask: Optional[np.ndarray] = None    # uint8 [B, D, D]: row i sees draft key j
+    sinks: Optional[np.ndarray] = None        # float32 [Hq]: sink logit per q head
+    logit_cap: float = 0.0                    # > 0: scores s -> cap * tanh(s / cap)
+
+    @property
+    def rows(self) -> int:
+        """Query rows: B*D, or qo_indptr[B] with ragged rows."""
+        return int(self.qo_indptr[-1]) if self.qo_indptr is not None else self.batch * self.draft_len
 
     @property
     def v_aliases_k(self) -> bool:
@@ -157,7 +168,9 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
                  v_aliases_k: bool = False, sm_scale: Optional[float] = None,
                  window_left: int = -1, num_splits: int = 0,
                  num_pages: Optional[int] = None, pool_factor: float = 1.25,
-                 seed: int = 0, poison: bool = False, shuffle_pages: bool = True) -> Problem:
+                 seed: int = 0, poison: bool = False, shuffle_pages: bool = True,
+                 draft_counts=None, ragged: bool = False, tree: bool = False,
+                 sinks: bool = False, logit_cap: float = 0.0) -> Problem:
     """Draw one problem.
 
     ``prefix_lens``: explicit list, or ``prefix_range=(lo, hi)`` for
@@ -167,12 +180,22 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
     sequence's last page) holds NaN bit patterns.  ``shuffle_pages=False`` hands
     out pages in pool order (each sequence's pages contiguous), the layout a
     fresh allocator would produce.
+
+    Extensions (each drawn from its own child stream, so the base arrays do not
+    change): ``ragged`` (or explicit ``draft_counts``) gives sequence b n_b draft
+    rows, uniform in [1, D], laid out by ``qo_indptr``; ``tree`` keeps the token
+    list to the prefix and puts the D draft keys of each sequence at scattered
+    slots of extra pages, with a random tree (each draft's parent is an earlier
+    draft or the prefix) whose ancestor-or-self relation is ``tree_mask``;
+    ``sinks`` draws one N(0, 1) sink logit per q head; ``logit_cap`` is passed on.
     """
     v_dim = qk_dim if v_dim is None else v_dim
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(qk_dim)
-    kids = np.random.SeedSequence(seed).spawn(4)
+    kids = np.random.SeedSequence(seed).spawn(7)
     rng = np.random.default_rng(kids[0])
+    if tree and (ragged or draft_counts is not None or window_left >= 0):
+        raise ValueError("tree verify takes uniform rows and no window")
 
     # 1. prefix lengths
     if prefix_lens is not None:
@@ -181,9 +204,19 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
         lens = rng.integers(prefix_range[0], prefix_range[1] + 1, size=batch).astype(np.int64)
     else:
         raise ValueError("give prefix_lens or prefix_range")
-    n_tok = lens + draft_len
+    if draft_counts is not None:
+        nq = np.asarray(draft_counts, dtype=np.int64).reshape(batch)
+    elif ragged:
+        nq = np.random.default_rng(kids[4]).integers(1, draft_len + 1, size=batch).astype(np.int64)
+    else:
+        nq = np.full(batch, draft_len, dtype=np.int64)
+    if (ragged or draft_counts is not None) and ((nq < 1).any() or (nq > draft_len).any()):
+        raise ValueError("draft counts must be in [1, draft_len]")
+    # token list: prefix then the sequence's draft tokens (tree: prefix only)
+    n_tok = lens if tree else lens + nq
     n_pages = -(-n_tok // page_size)
-    total_pages = int(n_pages.sum())
+    d_pages = -(-draft_len // page_size) if tree else 0   # tree: pages holding draft keys
+    total_pages = int(n_pages.sum()) + batch * d_pages
 
     # 2. page permutation: each sequence's pages, in order, from a shuffled pool
     reserved = 1 if poison else 0
@@ -206,11 +239,26 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
         t = np.arange(n_tok[b], dtype=np.int64)
         indices[indptr[b]: indptr[b] + n_tok[b]] = pg[t // page_size] * page_size + t % page_size
         indptr[b + 1] = indptr[b] + n_tok[b]
+    draft_slots = tree_mask = None
+    if tree:
+        trng = np.random.default_rng(kids[5])
+        dpg = perm[off: off + batch * d_pages].astype(np.int64)
+        cand = (dpg[:, None] * page_size + np.arange(page_size)[None, :]).reshape(-1)
+        draft_slots = trng.permutation(cand)[: batch * draft_len].reshape(batch, draft_len)
+        tree_mask = np.zeros((batch, draft_len, draft_len), dtype=np.uint8)
+        for b in range(batch):
+            parent = [-1] + [int(trng.integers(-1, j)) for j in range(1, draft_len)]
+            for i in range(draft_len):
+                a = i
+                while a >= 0:          # ancestors and self
+                    tree_mask[b, i, a] = 1
+                    a = parent[a]
 
     # 3-5. q, then the owned pages of the K and V pools (in page-id order)
     num_slots = num_pages * page_size
-    q = _normal_encoded(kids[1], batch * draft_len * hq * qk_dim, KV_BF16, 1.0)
-    q = q.reshape(batch * draft_len, hq, qk_dim)
+    n_rows = int(nq.sum())
+    q = _normal_encoded(kids[1], n_rows * hq * qk_dim, KV_BF16, 1.0)
+    q = q.reshape(n_rows, hq, qk_dim)
     owned_pages = np.sort(perm)
 
     def pool(seq, width):
@@ -227,6 +275,8 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
     if poison:
         owned = np.zeros(num_slots, dtype=bool)
         owned[indices] = True
+        if draft_slots is not None:
+            owned[draft_slots.reshape(-1)] = True
         nan = E4M3FN_NAN_BITS if kv_dtype == KV_FP8_E4M3FN else BF16_NAN_BITS
         k[~owned] = nan
         if v is not None:
@@ -240,7 +290,14 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
         sm_scale=float(sm_scale), window_left=int(window_left), num_splits=int(num_splits),
         prefix_lens=lens.astype(np.int32), kv_indptr=indptr.astype(np.int32),
         kv_indices=indices.astype(np.int32), page_ids=page_ids, num_pages=int(num_pages),
-        q=q, k_cache=k, v_cache=v, seed=seed)
+        q=q, k_cache=k, v_cache=v, seed=seed,
+        qo_indptr=(np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+                   if (ragged or draft_counts is not None) else None),
+        draft_slots=None if draft_slots is None else draft_slots.astype(np.int32),
+        tree_mask=tree_mask,
+        sinks=(np.random.default_rng(kids[6]).standard_normal(hq).astype(np.float32)
+               if sinks else None),
+        logit_cap=float(logit_cap))
 
 
 # The five workloads.  Shapes follow the pages' serving settings: 4 draft tokens at

@@ -408,3 +408,186 @@ def test_verify_bandwidth_figure_from_pages():
     p.qk_dim = p.v_dim = int(g["head_dim"])
     mb = W.algorithmic_kv_bytes(p) / 1e6
     assert abs(mb - g["kv_bytes_mb"]) / g["kv_bytes_mb"] < 0.005
+
+
+# ---------------------------------------------------------------------------
+# extensions: ragged rows, tree verify, sinks, logit cap, window-pool slots
+# ---------------------------------------------------------------------------
+
+def _rows_of(p, b):
+    qo = p.qo_indptr
+    return list(range(int(qo[b]), int(qo[b + 1])))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ragged_rows_match_full_causal_sdpa(seed):
+    # sequence b's n_b rows are the last n_b tokens of its KV; a square causal
+    # mask over [prefix; rows] fixes the alignment without any choice of ours
+    p = small(seed=500 + seed, batch=4, prefix_range=(0, 30), ragged=True)
+    O, LSE = oracle.run(p)
+    rng = np.random.default_rng(seed)
+    for b in range(p.batch):
+        rows = _rows_of(p, b)
+        K, V = dense_sequence(p, b)
+        n = K.shape[1]
+        L = int(p.prefix_lens[b])
+        assert n == L + len(rows)
+        Q = torch.from_numpy(rng.standard_normal((p.hq, n, p.qk_dim)))
+        Q[:, L:] = t_decode(p.q[rows], W.KV_BF16).permute(1, 0, 2)
+        ref = F.scaled_dot_product_attention(Q[None], K[None], V[None], is_causal=True,
+                                             scale=p.sm_scale, enable_gqa=True)[0]
+        np.testing.assert_allclose(O[rows], ref[:, L:].permute(1, 0, 2).numpy(),
+                                   rtol=1e-12, atol=1e-12)
+    assert np.isfinite(LSE).all()
+
+
+def test_ragged_with_full_counts_is_uniform():
+    p = small(seed=510, batch=3, prefix_range=(0, 30))
+    pr = small(seed=510, batch=3, prefix_range=(0, 30), draft_counts=[4, 4, 4])
+    O, LSE = oracle.run(p)
+    Or, LSEr = oracle.run(pr)
+    assert np.array_equal(pr.qo_indptr, [0, 4, 8, 12])
+    np.testing.assert_array_equal(O, Or)
+    np.testing.assert_array_equal(LSE, LSEr)
+
+
+def _tree_dense(p, b):
+    """[prefix; drafts] K, V of sequence b as dense [Hkv, L + D, d], drafts by their slots."""
+    K, V = dense_sequence(p, b)                    # prefix only in tree mode
+    ds = p.draft_slots[b].astype(np.int64)
+    Kd = (t_decode(p.k_cache[ds, :, : p.qk_dim], p.kv_dtype) * p.k_scale).permute(1, 0, 2)
+    Vd = (t_decode(p.v_view()[ds, :, : p.v_dim], p.kv_dtype) * p.v_scale).permute(1, 0, 2)
+    return torch.cat([K, Kd], dim=1), torch.cat([V, Vd], dim=1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tree_mask_matches_sdpa_custom_mask(seed):
+    p = small(seed=520 + seed, batch=3, prefix_range=(0, 30), tree=True)
+    O, _ = oracle.run(p)
+    for b in range(p.batch):
+        K, V = _tree_dense(p, b)
+        L = int(p.prefix_lens[b])
+        mask = torch.zeros(p.draft_len, L + p.draft_len, dtype=torch.bool)
+        mask[:, :L] = True
+        mask[:, L:] = torch.from_numpy(p.tree_mask[b].astype(bool))
+        ref = F.scaled_dot_product_attention(draft_queries(p, b)[None], K[None], V[None],
+                                             attn_mask=mask, scale=p.sm_scale,
+                                             enable_gqa=True)[0]
+        np.testing.assert_allclose(O[b * p.draft_len:(b + 1) * p.draft_len],
+                                   ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_chain_tree_is_topk1_causal():
+    # a chain tree (draft j's parent is j-1) over draft slots equal to the token
+    # list's draft slots reproduces the topk = 1 result
+    p = small(seed=530, batch=3, prefix_range=(0, 30))
+    O, LSE = oracle.run(p)
+    D = p.draft_len
+    slots = np.stack([p.kv_indices[p.kv_indptr[b + 1] - D: p.kv_indptr[b + 1]]
+                      for b in range(p.batch)])
+    chain = np.tril(np.ones((D, D), dtype=np.uint8))[None].repeat(p.batch, 0)
+    Ot, LSEt = oracle.verify_attention(**oracle.problem_fields(p), draft_slots=slots, tree_mask=chain)
+    np.testing.assert_allclose(Ot, O, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(LSEt, LSE, rtol=1e-13, atol=1e-13)
+
+
+def test_sinks_match_sdpa_with_zero_value_key():
+    # the sink is one more key whose score is the sink logit (an additive mask bias
+    # on a zero key) and whose value is zero
+    p = small(seed=540, batch=3, prefix_range=(0, 30), sinks=True)
+    O, LSE = oracle.run(p)
+    for b in range(p.batch):
+        K, V = dense_sequence(p, b)
+        hkv, n, _ = K.shape
+        L = int(p.prefix_lens[b])
+        K2 = torch.cat([torch.zeros(hkv, 1, p.qk_dim, dtype=K.dtype), K], dim=1)
+        V2 = torch.cat([torch.zeros(hkv, 1, p.v_dim, dtype=V.dtype), V], dim=1)
+        bias = torch.full((p.hq, p.draft_len, n + 1), -math.inf, dtype=torch.float64)
+        causal = causal_mask(L, p.draft_len)
+        bias[:, :, 1:] = torch.where(causal, 0.0, -math.inf)
+        bias[:, :, 0] = torch.from_numpy(p.sinks.astype(np.float64))[:, None]
+        ref = F.scaled_dot_product_attention(draft_queries(p, b)[None], K2[None], V2[None],
+                                             attn_mask=bias[None], scale=p.sm_scale,
+                                             enable_gqa=True)[0]
+        np.testing.assert_allclose(O[b * p.draft_len:(b + 1) * p.draft_len],
+                                   ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    # a sink of -inf is no sink
+    p2 = small(seed=540, batch=3, prefix_range=(0, 30))
+    p2.sinks = np.full(p2.hq, -np.inf, dtype=np.float32)
+    np.testing.assert_allclose(oracle.run(p2)[0], oracle.run(small(seed=540, batch=3,
+                                                                   prefix_range=(0, 30)))[0],
+                               rtol=1e-14, atol=1e-15)
+
+
+def test_sink_raises_lse_by_its_share():
+    # LSE with a sink = log(exp(LSE without) + exp(sink)): the sink is one more
+    # term of the denominator
+    p = small(seed=545, batch=2, prefix_range=(0, 30), sinks=True)
+    _, LSE = oracle.run(p)
+    q = small(seed=545, batch=2, prefix_range=(0, 30))
+    _, LSE0 = oracle.run(q)
+    np.testing.assert_allclose(LSE, np.logaddexp(LSE0, p.sinks.astype(np.float64)[None, :]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_logit_cap_limits():
+    base = dict(seed=550, batch=3, prefix_range=(0, 30))
+    O0, LSE0 = oracle.run(small(**base))
+    # a huge cap leaves the scores (to rounding)
+    Ob, LSEb = oracle.run(small(**base, logit_cap=1e9))
+    np.testing.assert_allclose(Ob, O0, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(LSEb, LSE0, rtol=1e-9, atol=1e-9)
+    # a tiny cap flattens every score to ~0: O is the plain mean of the visible V
+    # rows and LSE = log(number of visible keys)
+    p = small(**base, logit_cap=1e-12)
+    O, LSE = oracle.run(p)
+    for b in range(p.batch):
+        K, V = dense_sequence(p, b)
+        L = int(p.prefix_lens[b])
+        for i in range(p.draft_len):
+            n = L + i + 1
+            mean = V[:, :n].mean(dim=1).numpy()                       # [Hkv, dv]
+            want = np.repeat(mean, p.hq // p.hkv, axis=0)
+            np.testing.assert_allclose(O[b * p.draft_len + i], want, rtol=1e-9, atol=1e-9)
+            np.testing.assert_allclose(LSE[b * p.draft_len + i], math.log(n), atol=1e-9)
+
+
+def test_logit_cap_bounds_weight_ratio():
+    # capped scores lie in (-cap, cap), so inside one row no key outweighs another
+    # by more than e^(2 cap): with a planted huge score the planted key's weight
+    # stays below e^(2 cap) / (e^(2 cap) + n - 1)
+    p = small(seed=560, batch=1, prefix_lens=[20], hq=2, hkv=1, logit_cap=1.0)
+    p.q[:] = 0
+    p.q[:, :, 0] = W._bf16_bits(np.array([30.0]))[0]        # huge score only with key dim 0
+    kf = p.k_cache.copy()
+    kf[:, :, :] = 0
+    s = int(p.kv_indices[p.kv_indptr[0] + 3])                  # key 3 of the sequence
+    kf[s, :, 0] = W._bf16_bits(np.array([30.0]))[0]
+    p.k_cache = kf
+    v = p.v_cache.copy()
+    v[:] = 0
+    v[s, :, 0] = W._bf16_bits(np.array([1.0]))[0]              # O[:, 0] = weight of key 3
+    p.v_cache = v
+    O, _ = oracle.run(p)
+    for i in range(p.draft_len):
+        n = 20 + i + 1
+        bound = math.exp(2.0) / (math.exp(2.0) + n - 1)
+        assert 0.0 < O[i, 0, 0] <= bound + 1e-12
+
+
+def test_window_pool_translation():
+    # identity map leaves the slots; a page-preserving map (pages permuted, offsets
+    # kept) commutes with the block-table transform
+    p = small(seed=570, batch=3, prefix_range=(0, 60), page_size=4)
+    ident = np.arange(p.num_slots)
+    np.testing.assert_array_equal(oracle.translate_slots(p.kv_indices, ident), p.kv_indices)
+    rng = np.random.default_rng(0)
+    pmap = rng.permutation(p.num_pages)
+    full_to_swa = (pmap[np.arange(p.num_slots) // 4] * 4 + np.arange(p.num_slots) % 4)
+    tr = oracle.translate_slots(p.kv_indices, full_to_swa)
+    bt, lens = oracle.block_table(p.kv_indptr, tr, 4, p.max_pages_per_seq)
+    bt0, lens0 = oracle.block_table(p.kv_indptr, p.kv_indices, 4, p.max_pages_per_seq)
+    for b in range(p.batch):
+        npg = -(-int(lens0[b]) // 4)
+        np.testing.assert_array_equal(bt[b, :npg], pmap[bt0[b, :npg]])
+    np.testing.assert_array_equal(lens, lens0)
