@@ -40,6 +40,7 @@
 #ifndef VERIFY_ATTN_H
 #define VERIFY_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -60,7 +61,8 @@ extern "C" {
 
 /*
  * Arguments of verify_attn_fwd / verify_attn_combine / verify_attn_can_handle.
- * Plain C struct passed by pointer; struct_size must be sizeof(verify_attn_args).
+ * Plain C struct passed by pointer; struct_size must be sizeof(verify_attn_args)
+ * or VERIFY_ATTN_ARGS_V1_SIZE.
  * All strides are in ELEMENTS of the pointed-to type; the innermost dimension of
  * every tensor is contiguous.  q and out are indexed by query row r = b*D + i
  * (the uniform-draft qo_indptr of PR #23146).
@@ -116,7 +118,34 @@ typedef struct verify_attn_args {
     int64_t o_stride_row, o_stride_head;
     /* lse: [B*D, hq] fp32 contiguous natural-log LSE of the scaled scores, or NULL     */
     float* lse;
+
+    /* ---- version 2: optional extensions.  A caller passing struct_size =
+       VERIFY_ATTN_ARGS_V1_SIZE (the layout up to here) gets none of them; with
+       sizeof(verify_attn_args), NULL / 0 turns each off. ----                          */
+    /* Ragged draft rows (draft-extend: rows = accept_length + 1 per sequence, the
+       cu_seqlens_q of PR #12128's draft-extend replay metadata, "Code Review"): [B+1] int32 device,
+       non-decreasing from 0; sequence b owns q/out/lse rows qo_indptr[b] ..
+       qo_indptr[b+1]-1, n_b <= draft_len of them, at positions L_b .. L_b+n_b-1
+       (its KV holds L_b + n_b tokens).  NULL: n_b = draft_len, row b*D + i.      */
+    const int32_t* qo_indptr;
+    /* Tree verify (topk > 1, left to a later change by PR #5168): draft key j of
+       sequence b sits at slot draft_slots[b*D + j] ([B, D] int32 device) instead of
+       after the prefix in the block table, and row i sees it iff
+       tree_mask[(b*D + i)*D + j] != 0 ([B, D, D] uint8 device).  The block table
+       then only needs the prefix.  Requires window_left = -1 and qo_indptr = NULL. */
+    const int32_t* draft_slots;
+    const uint8_t* tree_mask;
+    /* Attention sinks: [hq] fp32 device, one extra logit per q head (natural-log
+       units of the scaled scores) in every row's softmax denominator with a zero
+       value; lse includes it.  NULL: none.                                         */
+    const float* sinks;
+    /* Logit cap: > 0 replaces each scaled score s by cap * tanh(s / cap) (sinks are
+       not capped); 0: off.                                                         */
+    float logit_cap;
 } verify_attn_args;
+
+/* Size of the version 1 layout (every field before qo_indptr). */
+#define VERIFY_ATTN_ARGS_V1_SIZE ((int32_t)offsetof(verify_attn_args, qo_indptr))
 
 /*
  * Block-table scatter (PR #23146 page-table scatter kernels; validity at topk = 1
@@ -193,10 +222,25 @@ int32_t verify_attn_num_splits(const verify_attn_args* args);
 int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int32_t draft_len,
                                     int32_t v_dim, int32_t num_splits);
 
+/*
+ * Sliding-window pool slots (the unified-attention page's
+ * translate_loc_from_full_to_swa before the page-table transform): for i < n,
+ *     out[i] = full_to_swa[in[i]]
+ * so layers with a separate sliding-window KV pool can build their block table
+ * (verify_attn_build_block_table on `out`) from the full pool's token list.
+ *   in          [n] int32 device full-pool slots, each in [0, map_len)
+ *   full_to_swa [map_len] int32 device map
+ *   out         [n] int32 device, written (may not alias in)
+ * Errors: VA_EINVAL for n < 0, map_len < 1 or null pointers with n > 0.  Values of
+ * `in` outside [0, map_len) are a precondition violation (not detected).
+ */
+int verify_attn_translate_slots(const int32_t* in, int64_t n, const int32_t* full_to_swa,
+                                int64_t map_len, int32_t* out, void* stream);
+
 /* Text for a status code (static storage). */
 const char* verify_attn_strerror(int status);
 
-/* ABI version: bumps when verify_attn_args changes layout.  This header is version 1. */
+/* ABI version: bumps when verify_attn_args changes layout.  This header is version 2. */
 int32_t verify_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -37,9 +37,9 @@ Readings taken where the pages are silent (each is listed with its status):
   8. Block-table padding is page id 0 (parity unpinned by the pages: convention).
 
 Extensions beyond topk = 1 (the split-KV page lists them as what its fast path
-leaves to the fallback: sinks, logit cap, ragged extend; the overlap-spec page
-covers draft-extend with ``cu_seqlens_q`` from ``accept_length``; the page-size
-page leaves topk > 1 to a later change; the unified-attention page translates
+leaves to the fallback in "Modifications": sinks, logit cap, ragged extend;
+PR #12128's review builds draft-extend ``cu_seqlens_q`` from ``accept_length``;
+PR #5168 leaves topk > 1 to a later change; PR #23146's page-table code translates
 full-pool slots to a sliding-window pool):
   9. Ragged rows (draft-extend): sequence b owns the query rows
      qo_indptr[b] .. qo_indptr[b+1]-1, n_b of them, the last n_b tokens of its KV

@@ -29,6 +29,7 @@ EXPORTED = (
     "verify_attn_workspace_bytes",
     "verify_attn_strerror",
     "verify_attn_abi_version",
+    "verify_attn_translate_slots",
 )
 
 
@@ -69,7 +70,17 @@ class VerifyAttnArgs(ctypes.Structure):
         ("o_stride_row", ctypes.c_int64),
         ("o_stride_head", ctypes.c_int64),
         ("lse", ctypes.c_void_p),
+        # version 2 extensions
+        ("qo_indptr", ctypes.c_void_p),
+        ("draft_slots", ctypes.c_void_p),
+        ("tree_mask", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+        ("logit_cap", ctypes.c_float),
     ]
+
+
+# size of the version 1 layout (every field before qo_indptr)
+V1_SIZE = VerifyAttnArgs.qo_indptr.offset
 
 
 class VerifyAttnError(RuntimeError):
@@ -108,6 +119,8 @@ def load(path: Optional[str] = None):
     lib.verify_attn_strerror.restype = ctypes.c_char_p
     lib.verify_attn_abi_version.argtypes = []
     lib.verify_attn_abi_version.restype = i32
+    lib.verify_attn_translate_slots.argtypes = [vp, i64, vp, i64, vp, vp]
+    lib.verify_attn_translate_slots.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -176,7 +189,8 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
               sm_scale: float, max_prefix_len: int, out, workspace, lse=None,
               kv_dtype: int = VA_KV_BF16, k_scale: float = 1.0, v_scale: float = 1.0,
               window_left: int = -1, num_splits: int = 0, v_dim: Optional[int] = None,
-              qk_dim: Optional[int] = None) -> VerifyCall:
+              qk_dim: Optional[int] = None, qo_indptr=None, draft_slots=None, tree_mask=None,
+              sinks=None, logit_cap: float = 0.0) -> VerifyCall:
     """Build verify_attn_args from torch tensors.
 
     q [B*D, Hq, qk_dim] bf16; k_cache [num_slots, Hkv, >= qk_dim] and v_cache
@@ -184,7 +198,10 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
     k_cache itself (MLA alias, give v_dim); block_table [B, max_pages] int32;
     prefix_lens [B] int32; out [B*D, Hq, v_dim] bf16; workspace a float32 tensor of
     at least workspace_bytes() (or None while sizing it: see set_workspace); lse
-    [B*D, Hq] float32 or None."""
+    [B*D, Hq] float32 or None.  Extensions (include/verify_attn.h, version 2):
+    qo_indptr [B+1] int32 (ragged rows; q/out/lse then have qo_indptr[B] rows),
+    draft_slots [B, D] int32 with tree_mask [B, D, D] uint8 (tree verify), sinks
+    [Hq] float32, logit_cap."""
     qk_dim = q.shape[-1] if qk_dim is None else qk_dim
     v_dim = out.shape[-1] if v_dim is None else v_dim
     a = VerifyAttnArgs()
@@ -217,8 +234,15 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
     a.out = _ptr(out)
     a.o_stride_row, a.o_stride_head = out.stride(0), out.stride(1)
     a.lse = _ptr(lse)
+    a.qo_indptr = _ptr(qo_indptr)
+    a.draft_slots = _ptr(draft_slots)
+    a.tree_mask = _ptr(tree_mask)
+    a.sinks = _ptr(sinks)
+    a.logit_cap = float(logit_cap)
     return VerifyCall(a, dict(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
-                              prefix_lens=prefix_lens, out=out, workspace=workspace, lse=lse))
+                              prefix_lens=prefix_lens, out=out, workspace=workspace, lse=lse,
+                              qo_indptr=qo_indptr, draft_slots=draft_slots, tree_mask=tree_mask,
+                              sinks=sinks))
 
 
 def verify_attn_fwd(call: VerifyCall, stream=None, check=True) -> int:
@@ -249,6 +273,19 @@ def set_workspace(call: VerifyCall, workspace) -> None:
     call.args.workspace = _ptr(workspace)
     call.args.workspace_bytes = workspace.numel() * workspace.element_size()
     call.tensors["workspace"] = workspace
+
+
+def verify_attn_translate_slots(slots, full_to_swa, out=None, stream=None, check=True):
+    """out[i] = full_to_swa[slots[i]] on the GPU (int32 tensors); returns out."""
+    import torch
+    if out is None:
+        out = torch.empty_like(slots)
+    st = load().verify_attn_translate_slots(_ptr(slots), slots.numel(), _ptr(full_to_swa),
+                                            full_to_swa.numel(), _ptr(out), _stream_ptr(stream))
+    if not check:
+        return st
+    _check("verify_attn_translate_slots", st)
+    return out
 
 
 def verify_attn_workspace_bytes(batch, hkv, hq, draft_len, v_dim, num_splits) -> int:

@@ -46,4 +46,28 @@ int launch_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int3
                        stream);
 }
 
+// Sliding-window pool slots (PR #23146 page-table code: full-pool locations are
+// translated to the window pool before the table transform): out[i] =
+// full_to_swa[in[i]], one thread per entry.
+struct TranslateParams {
+  const int32_t* in;
+  int64_t n;
+  const int32_t* map;
+  int32_t* out;
+};
+
+__global__ __launch_bounds__(256) void translate_slots_kernel(TranslateParams P) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < P.n) P.out[i] = P.map[P.in[i]];
+}
+
+int launch_translate_slots(const int32_t* in, int64_t n, const int32_t* full_to_swa, int32_t* out,
+                           hipStream_t stream) {
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffff) return VA_EUNSUPPORTED;
+  const TranslateParams p{in, n, full_to_swa, out};
+  return launch_kernel(reinterpret_cast<const void*>(&translate_slots_kernel),
+                       dim3((unsigned)blocks), dim3(256), p, stream);
+}
+
 }  // namespace va

@@ -7,7 +7,9 @@
 // columns; a workgroup holds 4 rows of one (sequence b, KV head g).  Per row:
 //   M = max of the pieces' LSEs, weights e^{LSE - M} (a piece in which the row
 //   sees no key has LSE = -inf and weight 0), out = weighted mean in bf16 (round
-//   to nearest even), lse = M + log(sum of weights).
+//   to nearest even), lse = M + log(sum of weights).  An attention sink is one
+//   more term with LSE = the sink logit and a zero output (the split-KV page's
+//   can_handle() lists sinks among what its fast path does not serve).
 // Every row sees at least its own draft key, so M and the final LSE are finite.
 
 #include <math.h>
@@ -24,6 +26,8 @@ struct CombineParams {
   int64_t o_srow, o_shead;   // elements
   float* lse;
   int hkv, group, draft, rows, slots;
+  const int32_t* qo_indptr;  // ragged rows, or NULL (row b*D + i)
+  const float* sinks;        // [hq] sink logits, or NULL
 };
 
 namespace {
@@ -83,6 +87,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   if (row >= P.rows) return;  // no barriers in this kernel
+  const int i = row / P.group;
+  const int nrow_b = P.qo_indptr ? P.qo_indptr[b + 1] - P.qo_indptr[b] : P.draft;
+  if (i >= nrow_b) return;    // the sequence has fewer draft rows (draft-extend)
+  const int h = g * P.group + row % P.group;
+  const int r = (P.qo_indptr ? P.qo_indptr[b] : b * P.draft) + i;
 
   int n = P.counts[b];
   n = n < 1 ? 1 : (n > P.slots ? P.slots : n);
@@ -97,7 +106,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
 #pragma unroll
   for (int u = 0; u < NB; ++u)
     if (u < n) first[u] = load_cols<CPT>(po + u * pstride);
-  float M = -INFINITY;
+  // a sink joins the denominator as one more partial with a zero output
+  const float sink = P.sinks ? P.sinks[h] : -INFINITY;
+  float M = sink;
   for (int s0 = 0; s0 < n; s0 += 64) {
     const float ls = (s0 + lane < n) ? plse[(int64_t)(s0 + lane) * P.rows] : -INFINITY;
     M = fmaxf(M, wave_max(ls));
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   float acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
-  float Z = 0.f;
+  float Z = sink == -INFINITY ? 0.f : expf(sink - M);
   for (int s0 = 0; s0 < n; s0 += 64) {
     const float ls = (s0 + lane < n) ? plse[(int64_t)(s0 + lane) * P.rows] : -INFINITY;
     const float w = (ls == -INFINITY) ? 0.f : expf(ls - M);
@@ -132,9 +143,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
     }
   }
   const float invZ = 1.f / Z;
-  const int i = row / P.group;
-  const int h = g * P.group + row % P.group;
-  const int r = b * P.draft + i;
   uint16_t* op = P.out + (int64_t)r * P.o_srow + (int64_t)h * P.o_shead + lane * CPT;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) op[c] = f32_to_bf16_rne(acc[c] * invZ);
@@ -156,6 +164,8 @@ int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
   cp.draft = a->draft_len;
   cp.rows = p.rows;
   cp.slots = p.slots;
+  cp.qo_indptr = a->qo_indptr;
+  cp.sinks = a->sinks;
   const dim3 grid((p.rows + kWaves - 1) / kWaves, a->hkv, a->batch);
 #define VA_LAUNCH(DV_) \
   return launch_kernel(reinterpret_cast<const void*>(&combine_kernel<DV_>), grid, dim3(256), cp, st)

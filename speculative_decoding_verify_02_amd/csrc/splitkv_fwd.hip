@@ -93,14 +93,6 @@ struct KVRegs {
   uint32_t v[4 * G::TB / 16][G::VW];  // V groups of the lane's score-slot tokens
 };
 
-// Slot of token t0 + (lane % tb), clamped to the piece's last token: one page-id
-// load per lane covers a whole block; other lanes read it with ds_bpermute.
-__device__ __forceinline__ int lane_slot(const int32_t* bt_row, int t0, int t_last, int lane,
-                                         int tb, int lg, int pmask) {
-  const int t = min(t0 + (lane & (tb - 1)), t_last);
-  return (bt_row[t >> lg] << lg) | (t & pmask);
-}
-
 // Token of S^T slot i (0 .. 4*TT-1) of lane group j: the 16x16 accumulator of token
 // tile tt holds tokens 16*tt + 4*j + r (r = 0..3) in a lane.  P^T and V^T use the
 // same slot order, which is all the MFMA reduction needs.
@@ -154,12 +146,22 @@ struct RowState {
   f32x4 o[RT][DV / 16];
 };
 
-template <class G, bool FP8, int RT, int DV>
+// Per-piece key masks of a wave's RT row tiles (lane's row n of each).
+template <int RT>
+struct RowMask {
+  int lo[RT], hi[RT];   // key range p - W .. p of the row (p = L + i)
+  uint32_t bits[RT];    // tree verify: draft keys the row sees
+  int L;                // first draft key
+  bool tree;
+  float c_log2;         // sm_scale * k_scale * log2(e)
+  float cap;            // logit cap (0: off)
+};
+
+template <class G, bool FP8, int RT, int DV, bool EXT>
 __device__ __forceinline__ void compute_block(const uint8_t* tile, const KVRegs<G>& R,
                                               const bf16x8 (&qB)[RT][G::KSTEPS],
-                                              const int (&row_lo)[RT], const int (&row_hi)[RT],
-                                              RowState<DV, RT>& st, int t0, float c_log2, int n,
-                                              int j) {
+                                              const RowMask<RT>& mk, RowState<DV, RT>& st, int t0,
+                                              int n, int j) {
   constexpr int TT = G::TB / 16;
   constexpr int NS = 4 * TT;  // scores per lane per row tile
   constexpr int CPL = G::CPL;
@@ -205,11 +207,19 @@ __device__ __forceinline__ void compute_block(const uint8_t* tile, const KVRegs<
 #pragma unroll
     for (int e = 0; e < NS; ++e) {
       const int t = t0 + 16 * (e >> 2) + 4 * j + (e & 3);
-      const bool ok = (t >= row_lo[rt]) && (t <= row_hi[rt]);
-      const float v = ok ? sacc[e >> 2][rt][e & 3] * c_log2 : -INFINITY;
-      sc[e] = v;
-      bmax = fmaxf(bmax, v);
+      bool ok;
+      if constexpr (EXT) ok = key_ok(t, mk.lo[rt], mk.hi[rt], mk.L, mk.bits[rt], mk.tree);
+      else ok = (t >= mk.lo[rt]) && (t <= mk.hi[rt]);
+      sc[e] = ok ? sacc[e >> 2][rt][e & 3] * mk.c_log2 : -INFINITY;
     }
+    if constexpr (EXT) {
+      if (mk.cap > 0.f) {
+#pragma unroll
+        for (int e = 0; e < NS; ++e) sc[e] = sc[e] == -INFINITY ? sc[e] : cap_log2(sc[e], mk.cap);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NS; ++e) bmax = fmaxf(bmax, sc[e]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
     const float m_new = fmaxf(st.m[rt], bmax);
@@ -276,7 +286,9 @@ __device__ __forceinline__ void compute_block(const uint8_t* tile, const KVRegs<
 
 }  // namespace
 
-template <int DK, int DV, bool FP8, int RT, int NRG, int NTL, int TT, bool PIPE, int WPE>
+// EXT: tree verify and logit cap compiled in (they cost registers the plain path
+// needs, so the plain instances leave them out).
+template <int DK, int DV, bool FP8, int RT, int NRG, int NTL, int TT, bool PIPE, int WPE, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void splitkv_fwd_kernel(FwdParams P) {
   using G = Geo<DK, DV, FP8, TT>;
@@ -316,17 +328,24 @@ void splitkv_fwd_kernel(FwdParams P) {
   // Q^T as the B operand: lane holds row n of each row tile, 8 consecutive k-slots.
   // Keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys).
   bf16x8 qB[RT][KSTEPS];
-  int row_lo[RT], row_hi[RT];
+  RowMask<RT> mk;
+  mk.L = L;
+  mk.tree = P.draft_slots != nullptr;
+  mk.c_log2 = P.c_log2;
+  mk.cap = P.logit_cap;
+  const int nrow_b = seq_rows(P, b), row0_b = seq_row0(P, b);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = (rg * RT + rt) * 16 + n;
-    const bool rv = head_ok && row < P.rows;
-    const int i = rv ? row / P.group : 0;
+    const int i0 = row / P.group;
+    const bool rv = head_ok && row < P.rows && i0 < nrow_b;
+    const int i = rv ? i0 : 0;
     const int hh = rv ? row % P.group : 0;
-    row_lo[rt] = P.window >= 0 ? L + i - P.window : INT_MIN;
-    row_hi[rt] = rv ? min(t_last, L + i) : -1;
+    mk.lo[rt] = P.window >= 0 ? L + i - P.window : INT_MIN;
+    mk.hi[rt] = rv ? (mk.tree ? t_last : min(t_last, L + i)) : -1;
+    mk.bits[rt] = (EXT && mk.tree && rv) ? tree_bits(P, b, i) : 0u;
     const uint8_t* qp =
-        P.q + (int64_t)(b * P.draft + i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
+        P.q + (int64_t)(row0_b + i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       // element offset of this lane's 8 k-slots; matches the K operand chunk layout
@@ -348,6 +367,13 @@ void splitkv_fwd_kernel(FwdParams P) {
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
   auto t0_of = [&](int bk) { return t_begin + bk * TB; };
+  // slot of key t0 + (lane % TB), clamped to the piece: one lookup per lane covers a
+  // whole block; other lanes read it with ds_bpermute
+  auto lslot = [&](int t0) {
+    const int t = min(t0 + (lane & (TB - 1)), t_last);
+    if constexpr (EXT) return key_slot(P, bt_row, b, L, t, lg, pmask);
+    else return (bt_row[t >> lg] << lg) | (t & pmask);
+  };
 
   // a3: this wave's blocks are tl, tl+NTL, ...
   int blk = tl;
@@ -355,34 +381,34 @@ void splitkv_fwd_kernel(FwdParams P) {
     if constexpr (PIPE) {
       // next block's K/V loads in flight while a block computes (register sets A/B)
       int sl_next = 0, sl_after = 0;
-      const int sl0 = lane_slot(bt_row, t0_of(blk), t_last, lane, TB, lg, pmask);
-      if (blk + NTL < nblk) sl_next = lane_slot(bt_row, t0_of(blk + NTL), t_last, lane, TB, lg, pmask);
+      const int sl0 = lslot(t0_of(blk));
+      if (blk + NTL < nblk) sl_next = lslot(t0_of(blk + NTL));
       KVRegs<G> A, Bk;
       load_block<G>(A, sl0, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
       stage_k<G>(A, tile, lane);
       for (;;) {
         const int b1 = blk + NTL, b2 = blk + 2 * NTL;
         if (b1 < nblk) load_block<G>(Bk, sl_next, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
-        if (b2 < nblk) sl_after = lane_slot(bt_row, t0_of(b2), t_last, lane, TB, lg, pmask);
-        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, row_hi, st, t0_of(blk), P.c_log2, n, j);
+        if (b2 < nblk) sl_after = lslot(t0_of(b2));
+        compute_block<G, FP8, RT, DV, EXT>(tile, A, qB, mk, st, t0_of(blk), n, j);
         if (b1 >= nblk) break;
         stage_k<G>(Bk, tile, lane);
         const int b3 = blk + 3 * NTL;
         if (b2 < nblk) load_block<G>(A, sl_after, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
-        if (b3 < nblk) sl_next = lane_slot(bt_row, t0_of(b3), t_last, lane, TB, lg, pmask);
-        compute_block<G, FP8, RT, DV>(tile, Bk, qB, row_lo, row_hi, st, t0_of(b1), P.c_log2, n, j);
+        if (b3 < nblk) sl_next = lslot(t0_of(b3));
+        compute_block<G, FP8, RT, DV, EXT>(tile, Bk, qB, mk, st, t0_of(b1), n, j);
         if (b2 >= nblk) break;
         stage_k<G>(A, tile, lane);
         blk = b2;
       }
     } else {
-      int sl = lane_slot(bt_row, t0_of(blk), t_last, lane, TB, lg, pmask);
+      int sl = lslot(t0_of(blk));
       for (; blk < nblk; blk += NTL) {
         KVRegs<G> A;
         load_block<G>(A, sl, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
-        if (blk + NTL < nblk) sl = lane_slot(bt_row, t0_of(blk + NTL), t_last, lane, TB, lg, pmask);
+        if (blk + NTL < nblk) sl = lslot(t0_of(blk + NTL));
         stage_k<G>(A, tile, lane);
-        compute_block<G, FP8, RT, DV>(tile, A, qB, row_lo, row_hi, st, t0_of(blk), P.c_log2, n, j);
+        compute_block<G, FP8, RT, DV, EXT>(tile, A, qB, mk, st, t0_of(blk), n, j);
       }
     }
   }
@@ -456,7 +482,7 @@ void splitkv_fwd_kernel(FwdParams P) {
   for (int rt = 0; rt < RT; ++rt) {
     if (tl != NTL - 1 || !head_ok) break;
     const int row = (rg * RT + rt) * 16 + n;
-    if (row >= P.rows) continue;
+    if (row >= P.rows || row / P.group >= nrow_b) continue;
     const float l = l_run[rt];
     const float inv = l > 0.f ? P.v_scale / l : 0.f;
     float* po = P.part_o + (split_id * P.rows + row) * DV;
@@ -484,7 +510,7 @@ namespace {
 // Kernel variant per wave layout.  d = 128: 32-token blocks, K/V double-buffered.
 // d = 256: 32-token blocks, single buffer (a second one would not fit beside the
 // 32x256 accumulator).  d = 576/512: 16-token blocks, single buffer.
-template <int DK, int DV, bool FP8>
+template <int DK, int DV, bool FP8, bool EXT>
 int launch_dims(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {
   constexpr int TT = DK >= 576 ? 1 : 2;
   constexpr bool PIPE = DK == 128;
@@ -492,7 +518,7 @@ int launch_dims(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {
 #define VA_LAUNCH(RT_, NRG_, NTL_)                                                              \
   return launch_kernel(reinterpret_cast<const void*>(                                           \
                            &splitkv_fwd_kernel<DK, DV, FP8, RT_, NRG_, NTL_, TT, PIPE,          \
-                                               (DK == 128 && RT_ == 1) ? 2 : 1>),               \
+                                               (DK == 128 && RT_ == 1) ? 2 : 1, EXT>),          \
                        grid, dim3(256), fp, st)
   const int key = p.rt * 100 + p.nrg * 10 + p.ntl;
   if constexpr (DV > 256) {
@@ -555,18 +581,26 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.min_q = p.min_q;
   fp.c_log2 = a->sm_scale * a->k_scale * kLog2e;
   fp.v_scale = a->v_scale;
+  fp.qo_indptr = a->qo_indptr;
+  fp.draft_slots = a->draft_slots;
+  fp.tree_mask = a->tree_mask;
+  fp.logit_cap = a->logit_cap;
   // grid: x = head groups (fastest, so the heads of one key range are read together),
   // y = key ranges of the balanced partition
   const dim3 grid(p.hg, p.nwy, 1);
   if (p.kind == kMlaFp8) return launch_splitkv_mla_fp8(fp, p, grid, st);
   if (p.kind == kTile) return launch_splitkv_tile(fp, a->qk_dim, p.hpc, p.nrg, grid, st);
   const bool f8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
-  if (a->qk_dim == 128) return f8 ? launch_dims<128, 128, true>(fp, p, grid, st)
-                                  : launch_dims<128, 128, false>(fp, p, grid, st);
-  if (a->qk_dim == 256) return f8 ? launch_dims<256, 256, true>(fp, p, grid, st)
-                                  : launch_dims<256, 256, false>(fp, p, grid, st);
-  if (a->qk_dim == 576) return f8 ? launch_dims<576, 512, true>(fp, p, grid, st)
-                                  : launch_dims<576, 512, false>(fp, p, grid, st);
+  const bool ext = a->draft_slots != nullptr || a->logit_cap > 0.f;
+#define VA_DIMS(DK_, DV_)                                                                   \
+  return f8 ? (ext ? launch_dims<DK_, DV_, true, true>(fp, p, grid, st)                      \
+                   : launch_dims<DK_, DV_, true, false>(fp, p, grid, st))                    \
+            : (ext ? launch_dims<DK_, DV_, false, true>(fp, p, grid, st)                     \
+                   : launch_dims<DK_, DV_, false, false>(fp, p, grid, st))
+  if (a->qk_dim == 128) VA_DIMS(128, 128);
+  if (a->qk_dim == 256) VA_DIMS(256, 256);
+  if (a->qk_dim == 576) VA_DIMS(576, 512);
+#undef VA_DIMS
   return VA_EUNSUPPORTED;
 }
 

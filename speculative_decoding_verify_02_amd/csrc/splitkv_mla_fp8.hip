@@ -125,8 +125,7 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
 
   const int row = wave * 16 + n;
-  const bool rv = row < P.rows;
-  const int row_i = rv ? row / P.group : 0;  // draft index of this lane's row
+  const bool tree = P.draft_slots != nullptr;
   const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
@@ -140,6 +139,9 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   const int t_last = t_end - 1;
   if (pc.count > 0 && g == 0 && tid == 0) P.counts[b] = pc.count;
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
+  // the lane's row: draft row_i of sequence b (rows past the sequence's count idle)
+  const bool rv = row < P.rows && row / P.group < seq_rows(P, b);
+  const int row_i = rv ? row / P.group : 0;
 
   // page ids of this wave's keys of tile k -> s_pid[k % 2][wave]: entry e is the
   // page of the wave's first key plus e, clamped to the table row
@@ -156,7 +158,9 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
     const int pbase = min(t0, t_last) >> lg;
     uint8_t* ring = s_ring[k & 1];
     const int tl = min(t0 + (lane & (kKPW - 1)), t_last);
-    const int slot_l = (s_pid[k & 1][wave][(tl >> lg) - pbase] << lg) | (tl & pmask);
+    int slot_l = (s_pid[k & 1][wave][(tl >> lg) - pbase] << lg) | (tl & pmask);
+    if (tree && t0 + kKPW - 1 >= L)   // tree verify: draft keys at their own slots
+      slot_l = tl >= L ? P.draft_slots[b * P.draft + (tl - L)] : slot_l;
 #pragma unroll
     for (int u = 0; u < kKPW; ++u) {
       const int slot = __builtin_amdgcn_readlane(slot_l, u);
@@ -180,7 +184,7 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   {
     const int hh = rv ? row % P.group : 0;
     const uint8_t* qp =
-        P.q + (int64_t)(b * P.draft + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
+        P.q + (int64_t)(seq_row0(P, b) + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
     for (int kb = 0; kb < kVRB / 128; ++kb) {
       u32x4 raw[4];
@@ -218,9 +222,13 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   }
   // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
   const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
-  const int row_hi = rv ? min(t_last, L + row_i) : -1;
+  const int row_hi = rv ? (tree ? t_last : min(t_last, L + row_i)) : -1;
+  const uint32_t tbits = (tree && rv) ? tree_bits(P, b, row_i) : 0u;
   // keys every row of the wave sees: tiles inside [wave_lo, wave_hi] need no masking
-  int wave_lo = rv ? row_lo : INT_MIN, wave_hi = rv ? row_hi : INT_MAX;
+  // (tree draft keys and capped logits always take the general path)
+  int wave_lo = rv ? row_lo : INT_MIN;
+  int wave_hi = rv ? (tree ? min(row_hi, L - 1) : row_hi) : INT_MAX;
+  if (P.logit_cap > 0.f) wave_hi = INT_MIN;
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) {
     wave_lo = max(wave_lo, __shfl_xor(wave_lo, off, 64));
@@ -297,10 +305,15 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const int t = t0 + slot_token(j, e);
-        const bool ok = (t >= row_lo) && (t <= row_hi);
+        const bool ok = key_ok(t, row_lo, row_hi, L, tbits, tree);
         sc[e] = ok ? sacc[e >> 2][e & 3] * P.c_log2 : -INFINITY;
-        bmax = fmaxf(bmax, sc[e]);
       }
+      if (P.logit_cap > 0.f) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) sc[e] = sc[e] == -INFINITY ? sc[e] : cap_log2(sc[e], P.logit_cap);
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) bmax = fmaxf(bmax, sc[e]);
     }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));

@@ -71,8 +71,6 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   PieceWalk pw;
   if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
   const int row = rg * 16 + n;
-  const bool rv = row < P.rows;
-  const int row_i = rv ? row / P.group : 0;  // draft index of this lane's row
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
 
@@ -85,12 +83,18 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   const int t_last = t_end - 1;
   if (pc.count > 0 && blockIdx.x == 0 && tid == 0) P.counts[b] = pc.count;
 
+  // the lane's row: draft row_i of sequence b (rows past the sequence's count idle)
+  const bool rv = row < P.rows && row / P.group < seq_rows(P, b);
+  const int row_i = rv ? row / P.group : 0;
+  const bool tree = P.draft_slots != nullptr;
+  const uint32_t tbits = (tree && rv) ? tree_bits(P, b, row_i) : 0u;
+
   // Q^T operands of this wave's 16 rows: k-step ks holds elements 32ks + 8j + [0, 8)
   bf16x8 qB[KS];
   {
     const int hh = rv ? row % P.group : 0;
-    const uint8_t* qp =
-        P.q + (int64_t)(b * P.draft + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
+    const uint8_t* qp = P.q + (int64_t)(seq_row0(P, b) + row_i) * P.q_srow +
+                        (int64_t)(g * P.group + hh) * P.q_shead;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   }
   // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
   const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
-  const int row_hi = rv ? min(t_last, L + row_i) : -1;
+  const int row_hi = rv ? (tree ? t_last : min(t_last, L + row_i)) : -1;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[CT];
@@ -110,8 +114,7 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
   // this thread's load chunks: q = 64*W*u + tid -> token q / CH, head (q % CH) / (RB/16)
   auto lane_slot = [&](int t0) {
-    const int t = min(t0 + (lane & (kTB - 1)), t_last);
-    return (bt_row[t >> lg] << lg) | (t & pmask);
+    return key_slot(P, bt_row, b, L, min(t0 + (lane & (kTB - 1)), t_last), lg, pmask);
   };
   // one register set holds the next block while this one computes
   u32x4 kr[G::NLD], vr[G::NLD];
@@ -172,10 +175,15 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + 4 * j + r;
-      const bool ok = (t >= row_lo) && (t <= row_hi);
+      const bool ok = key_ok(t, row_lo, row_hi, L, tbits, tree);
       sc[r] = ok ? sacc[r] * P.c_log2 : -INFINITY;
-      bmax = fmaxf(bmax, sc[r]);
     }
+    if (P.logit_cap > 0.f) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = sc[r] == -INFINITY ? sc[r] : cap_log2(sc[r], P.logit_cap);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, sc[r]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
     const float m_new = fmaxf(m_run, bmax);

@@ -58,14 +58,61 @@ struct FwdParams {
   int slots, min_q;
   float c_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
+  // extensions (NULL / 0: off)
+  const int32_t* qo_indptr;    // [B+1] ragged rows: sequence b has rows qo[b] .. qo[b+1]-1
+  const int32_t* draft_slots;  // [B, D] tree verify: slot of draft key j
+  const uint8_t* tree_mask;    // [B, D, D] tree verify: row i sees draft key j
+  float logit_cap;             // > 0: natural-log scores s -> cap * tanh(s / cap)
 };
+
+// Draft rows of sequence b and the q/out row of its first one.
+__device__ __forceinline__ int seq_rows(const FwdParams& P, int b) {
+  return P.qo_indptr ? P.qo_indptr[b + 1] - P.qo_indptr[b] : P.draft;
+}
+__device__ __forceinline__ int seq_row0(const FwdParams& P, int b) {
+  return P.qo_indptr ? P.qo_indptr[b] : b * P.draft;
+}
+
+// Slot of key t of sequence b: prefix keys (and, at topk = 1, draft keys) through
+// the block table; in tree verify the D draft keys t >= L through draft_slots.
+__device__ __forceinline__ int key_slot(const FwdParams& P, const int32_t* bt_row, int b, int L,
+                                        int t, int lg, int pmask) {
+  if (P.draft_slots && t >= L) return P.draft_slots[b * P.draft + (t - L)];
+  return (bt_row[t >> lg] << lg) | (t & pmask);
+}
+
+// Tree verify: the draft keys row i of sequence b sees, one bit per draft key.
+__device__ __forceinline__ uint32_t tree_bits(const FwdParams& P, int b, int i) {
+  uint32_t m = 0;
+  const uint8_t* r = P.tree_mask + ((int64_t)b * P.draft + i) * P.draft;
+  for (int jj = 0; jj < P.draft; ++jj) m |= (r[jj] ? 1u : 0u) << jj;
+  return m;
+}
+
+// Key t visible to a row with key range [lo, hi] (tree verify: draft keys t >= L by
+// the row's bits).
+__device__ __forceinline__ bool key_ok(int t, int lo, int hi, int L, uint32_t bits, bool tree) {
+  return (t >= lo) && (t <= hi) && (!tree || t < L || ((bits >> (t - L)) & 1u));
+}
+
+// Logit cap on a score in the exp2 domain: x = s * log2(e) with s natural-log, so the
+// capped value is cap * log2(e) * tanh(s / cap).  tanh(y) = (e - 1) / (e + 1) with
+// e = exp(2y) = 2^(2x / cap); |2x / cap| is clamped at 60, where tanh is 1 in fp32.
+// The absolute error of the capped score is a few ulp of cap.
+__device__ __forceinline__ float cap_log2(float x, float cap) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  const float z = fminf(fmaxf(x * (2.f / cap), -60.f), 60.f);
+  const float e = __builtin_amdgcn_exp2f(z);
+  return (cap * kLog2e) * (e - 1.f) * __builtin_amdgcn_rcpf(e + 1.f);
+}
 
 // ---------------------------------------------------------------------------
 // Work partition of the split-KV pass (device side, identical in every wave).
 //
-// Sequence b owns len_b = (L_b - lo_b) + D keys: its attended prefix [lo_b, L_b)
-// (lo_b = max(0, L_b - W) with a left window W, else 0) and then its D draft keys,
-// which sit in the paged cache right after the prefix.  The sequences' keys are
+// Sequence b owns len_b = (L_b - lo_b) + n_b keys: its attended prefix [lo_b, L_b)
+// (lo_b = max(0, L_b - W) with a left window W, else 0) and then its n_b draft keys
+// (n_b = D, or qo[b+1] - qo[b] with ragged rows), which sit in the paged cache
+// right after the prefix (tree verify: D draft keys at draft_slots).  The sequences' keys are
 // laid end to end (T in all) and cut into ranges of
 //     q = max(ceil(T / nwy), ceil(max_b len_b / (slots - 1)), min_q)
 // keys, range y going to the workgroups of grid row y (one per head group), so
@@ -99,6 +146,13 @@ __device__ __forceinline__ int seq_lo(const FwdParams& P, int L) {
   return P.window >= 0 ? max(0, L - P.window) : 0;
 }
 
+// Keys of sequence b's pieces: its attended prefix and its draft keys (none when it
+// has no rows).
+__device__ __forceinline__ int seq_len_keys(const FwdParams& P, int b, int L) {
+  const int n = seq_rows(P, b);
+  return n > 0 ? L - seq_lo(P, L) + (P.draft_slots ? P.draft : n) : 0;
+}
+
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
@@ -114,7 +168,7 @@ struct PieceWalk {
     const int lane = threadIdx.x & 63;
     y = row;
     if (P.slots == 1) {
-      if (y >= P.batch) return false;
+      if (y >= P.batch || seq_len_keys(P, y, seq_prefix_len(P, y)) == 0) return false;
       b = y;
       q = 0;
       return true;
@@ -123,10 +177,7 @@ struct PieceWalk {
     int mx = 0;
     for (int c = 0; c < P.batch; c += 64) {
       int l = 0;
-      if (c + lane < P.batch) {
-        const int L = seq_prefix_len(P, c + lane);
-        l = L - seq_lo(P, L) + P.draft;
-      }
+      if (c + lane < P.batch) l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
       int64_t sum = l;
       int m = l;
 #pragma unroll
@@ -152,10 +203,7 @@ struct PieceWalk {
     int64_t base = 0;
     for (int c = 0; c < P.batch; c += 64) {
       int l = 0;
-      if (c + lane < P.batch) {
-        const int L = seq_prefix_len(P, c + lane);
-        l = L - seq_lo(P, L) + P.draft;
-      }
+      if (c + lane < P.batch) l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
       int64_t incl = l;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -179,10 +227,10 @@ struct PieceWalk {
     pc.b = __builtin_amdgcn_readfirstlane(b);
     pc.L = __builtin_amdgcn_readfirstlane(seq_prefix_len(P, pc.b));
     const int lo = seq_lo(P, pc.L);
-    len = pc.L - lo + P.draft;
+    len = seq_len_keys(P, pc.b, pc.L);
     if (P.slots == 1) {
       pc.t0 = lo;
-      pc.t1 = pc.L + P.draft;
+      pc.t1 = lo + len;
       pc.slot = 0;
       pc.count = 1;
       return pc;
@@ -205,9 +253,13 @@ struct PieceWalk {
   __device__ bool next(const FwdParams& P) {
     if (P.slots == 1) return false;
     cum += len;
-    if (cum >= e || b + 1 >= P.batch) return false;
-    ++b;
-    return true;
+    // the next sequence with keys (sequences without rows own none)
+    while (cum < e && b + 1 < P.batch) {
+      ++b;
+      len = seq_len_keys(P, b, seq_prefix_len(P, b));
+      if (len > 0) return true;
+    }
+    return false;
   }
 };
 
@@ -226,6 +278,8 @@ int launch_splitkv_tile(const FwdParams& fp, int d, int hpc, int nrg, dim3 grid,
 // fp8 MLA heads (qk_dim 576, v_dim 512 = first 512 of the K row), <= 64 rows per head.
 int launch_splitkv_mla_fp8(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t stream);
 int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t stream);
+int launch_translate_slots(const int32_t* in, int64_t n, const int32_t* full_to_swa, int32_t* out,
+                           hipStream_t stream);
 
 // Compute-unit count of the current device (cached per device).
 int device_cu_count();

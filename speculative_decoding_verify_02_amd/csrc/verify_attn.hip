@@ -4,6 +4,8 @@
 // max-batch-keyed scratch follow the same rule).
 
 #include <math.h>
+#include <string.h>
+
 #include <mutex>
 
 #include "va_internal.h"
@@ -76,6 +78,10 @@ int device_cu_count() {
 
 int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
   if (!a || a->struct_size != (int32_t)sizeof(verify_attn_args)) return VA_EINVAL;
+  // extensions: a tree needs its mask, takes uniform rows and no window
+  if ((a->draft_slots == nullptr) != (a->tree_mask == nullptr)) return VA_EINVAL;
+  if (!(a->logit_cap >= 0.f) || !isfinite(a->logit_cap)) return VA_EINVAL;
+  if (a->draft_slots && (a->qo_indptr || a->window_left >= 0)) return VA_EUNSUPPORTED;
   if (a->batch < 0 || a->draft_len < 1 || a->hq < 1 || a->hkv < 1 || a->max_prefix_len < 0 ||
       a->num_splits < 0 || a->window_left < -1 || a->max_pages_per_seq < 1)
     return VA_EINVAL;
@@ -175,7 +181,7 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
 
 extern "C" {
 
-int32_t verify_attn_abi_version(void) { return 1; }
+int32_t verify_attn_abi_version(void) { return 2; }
 
 const char* verify_attn_strerror(int status) {
   switch (status) {
@@ -196,17 +202,31 @@ int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int3
   return ((int64_t)batch * hkv * num_splits * rows * ((int64_t)v_dim + 1) + batch) * 4;
 }
 
+// Copies the caller's arguments into a full current-version struct: a version 1
+// caller's struct ends before the extension fields, which then read as off.
+static int load_args(const verify_attn_args* in, verify_attn_args* out) {
+  if (!in) return VA_EINVAL;
+  const int32_t sz = in->struct_size;
+  if (sz != (int32_t)sizeof(verify_attn_args) && sz != VERIFY_ATTN_ARGS_V1_SIZE) return VA_EINVAL;
+  memset(out, 0, sizeof(*out));
+  memcpy(out, in, (size_t)sz);
+  out->struct_size = (int32_t)sizeof(verify_attn_args);
+  return VA_OK;
+}
+
 int32_t verify_attn_num_splits(const verify_attn_args* args) {
   va::Plan p;
-  if (!args) return -1;
-  verify_attn_args a = *args;
+  verify_attn_args a;
+  if (load_args(args, &a) != VA_OK) return -1;
   a.num_splits = 0;  // the heuristic's choice, whatever the caller asked for
   return va::make_plan(&a, &p, /*check_pointers=*/false) == VA_OK ? p.slots : -1;
 }
 
 int verify_attn_can_handle(const verify_attn_args* args) {
   va::Plan p;
-  return va::make_plan(args, &p, true);
+  verify_attn_args a;
+  const int st = load_args(args, &a);
+  return st != VA_OK ? st : va::make_plan(&a, &p, true);
 }
 
 static int check_workspace(const verify_attn_args* a, const va::Plan& p) {
@@ -217,22 +237,32 @@ static int check_workspace(const verify_attn_args* a, const va::Plan& p) {
 
 int verify_attn_fwd(const verify_attn_args* args, void* stream) {
   va::Plan p;
-  int st = va::make_plan(args, &p, true);
-  if (st != VA_OK) return st;
-  if ((st = check_workspace(args, p)) != VA_OK) return st;
-  // launched even when the host bound says no prefix is attended: a device length
-  // above the bound must still be covered (the last split absorbs it)
-  if (args->batch == 0) return VA_OK;
-  return va::launch_splitkv_fwd(args, p, reinterpret_cast<hipStream_t>(stream));
+  verify_attn_args a;
+  int st = load_args(args, &a);
+  if (st != VA_OK || (st = va::make_plan(&a, &p, true)) != VA_OK) return st;
+  if ((st = check_workspace(&a, p)) != VA_OK) return st;
+  // launched even when the host bound says no prefix is attended: the device lengths
+  // decide what each workgroup covers
+  if (a.batch == 0) return VA_OK;
+  return va::launch_splitkv_fwd(&a, p, reinterpret_cast<hipStream_t>(stream));
 }
 
 int verify_attn_combine(const verify_attn_args* args, void* stream) {
   va::Plan p;
-  int st = va::make_plan(args, &p, true);
-  if (st != VA_OK) return st;
-  if ((st = check_workspace(args, p)) != VA_OK) return st;
-  if (args->batch == 0) return VA_OK;
-  return va::launch_combine(args, p, reinterpret_cast<hipStream_t>(stream));
+  verify_attn_args a;
+  int st = load_args(args, &a);
+  if (st != VA_OK || (st = va::make_plan(&a, &p, true)) != VA_OK) return st;
+  if ((st = check_workspace(&a, p)) != VA_OK) return st;
+  if (a.batch == 0) return VA_OK;
+  return va::launch_combine(&a, p, reinterpret_cast<hipStream_t>(stream));
+}
+
+int verify_attn_translate_slots(const int32_t* in, int64_t n, const int32_t* full_to_swa,
+                                int64_t map_len, int32_t* out, void* stream) {
+  if (n < 0 || map_len < 1) return VA_EINVAL;
+  if (n == 0) return VA_OK;
+  if (!in || !full_to_swa || !out) return VA_EINVAL;
+  return va::launch_translate_slots(in, n, full_to_swa, out, reinterpret_cast<hipStream_t>(stream));
 }
 
 int verify_attn_build_block_table(const int32_t* kv_indptr, const int32_t* kv_indices,

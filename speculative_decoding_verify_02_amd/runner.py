@@ -49,9 +49,13 @@ class DeviceProblem:
         self.block_table = torch.empty((p.batch, self.max_pages), dtype=torch.int32,
                                        device=device)
         self.kv_lens = torch.empty((p.batch,), dtype=torch.int32, device=device)
-        self.out = torch.empty((p.batch * p.draft_len, p.hq, p.v_dim), dtype=torch.bfloat16,
-                               device=device)
-        self.lse = torch.empty((p.batch * p.draft_len, p.hq), dtype=torch.float32, device=device)
+        self.out = torch.empty((p.rows, p.hq, p.v_dim), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((p.rows, p.hq), dtype=torch.float32, device=device)
+        opt = lambda a: None if a is None else _to_dev(np.ascontiguousarray(a), device)
+        self.qo_indptr = opt(None if p.qo_indptr is None else p.qo_indptr.astype(np.int32))
+        self.draft_slots = opt(None if p.draft_slots is None else p.draft_slots.astype(np.int32))
+        self.tree_mask = opt(None if p.tree_mask is None else p.tree_mask.astype(np.uint8))
+        self.sinks = opt(None if p.sinks is None else p.sinks.astype(np.float32))
         ns = p.num_splits if num_splits is None else num_splits
         self.workspace = None
         self.calls = [self._make_call(c) for c in range(kv_copies)]
@@ -73,7 +77,9 @@ class DeviceProblem:
             draft_len=p.draft_len, page_size=p.page_size, sm_scale=p.sm_scale,
             max_prefix_len=p.max_prefix_len, out=self.out, workspace=self.workspace,
             lse=self.lse, kv_dtype=p.kv_dtype, k_scale=p.k_scale, v_scale=p.v_scale,
-            window_left=p.window_left, num_splits=0, qk_dim=p.qk_dim, v_dim=p.v_dim)
+            window_left=p.window_left, num_splits=0, qk_dim=p.qk_dim, v_dim=p.v_dim,
+            qo_indptr=self.qo_indptr, draft_slots=self.draft_slots, tree_mask=self.tree_mask,
+            sinks=self.sinks, logit_cap=p.logit_cap)
 
     def build_block_table(self, stream=None):
         binding.verify_attn_build_block_table(self.kv_indptr, self.kv_indices, self.p.page_size,

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(B.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.verify_attn_abi_version() == 1
+    assert lib.verify_attn_abi_version() == 2
 
 
 def fake_args(**kw):
@@ -97,6 +97,13 @@ def test_gate_accepts_supported_shapes():
     (dict(sm_scale=float("nan")), B.VA_EINVAL),
     (dict(k_scale=0.5), B.VA_EINVAL),                   # scales must be 1 for bf16
     (dict(kv_dtype=7), B.VA_EINVAL),
+    (dict(struct_size=B.V1_SIZE + 4), B.VA_EINVAL),     # neither layout
+    (dict(draft_slots=FAKE), B.VA_EINVAL),              # a tree needs its mask
+    (dict(tree_mask=FAKE), B.VA_EINVAL),
+    (dict(logit_cap=-1.0), B.VA_EINVAL),
+    (dict(logit_cap=float("inf")), B.VA_EINVAL),
+    (dict(draft_slots=FAKE, tree_mask=FAKE, window_left=8), B.VA_EUNSUPPORTED),
+    (dict(draft_slots=FAKE, tree_mask=FAKE, qo_indptr=FAKE), B.VA_EUNSUPPORTED),
     (dict(draft_len=9), B.VA_EUNSUPPORTED),
     (dict(qk_dim=64, v_dim=64), B.VA_EUNSUPPORTED),
     (dict(qk_dim=128, v_dim=256), B.VA_EUNSUPPORTED),
@@ -150,3 +157,26 @@ def test_host_helpers():
     assert lib.verify_attn_num_splits(ctypes.byref(fake_args(hq=7))) == -1
     for st in range(6):
         assert isinstance(B.strerror(st), str)
+
+
+def test_version1_layout_still_accepted():
+    # a caller built against the version 1 header passes the shorter struct size;
+    # the extension fields then read as off, whatever lies past its struct
+    a = fake_args(struct_size=B.V1_SIZE, draft_slots=FAKE, logit_cap=-5.0)
+    assert B.load().verify_attn_can_handle(ctypes.byref(a)) == B.VA_OK
+    assert B.load().verify_attn_num_splits(ctypes.byref(a)) >= 1
+
+
+def test_extensions_accepted():
+    assert can_handle(qo_indptr=FAKE) == B.VA_OK
+    assert can_handle(draft_slots=FAKE, tree_mask=FAKE) == B.VA_OK
+    assert can_handle(sinks=FAKE, logit_cap=30.0) == B.VA_OK
+
+
+def test_translate_slots_arguments():
+    lib = B.load()
+    assert lib.verify_attn_translate_slots(None, 0, None, 1, None, None) == B.VA_OK
+    assert lib.verify_attn_translate_slots(FAKE, -1, FAKE, 1, FAKE, None) == B.VA_EINVAL
+    assert lib.verify_attn_translate_slots(FAKE, 4, FAKE, 0, FAKE, None) == B.VA_EINVAL
+    assert lib.verify_attn_translate_slots(None, 4, FAKE, 8, FAKE, None) == B.VA_EINVAL
+    assert lib.verify_attn_translate_slots(FAKE, 4, FAKE, 8, None, None) == B.VA_EINVAL

@@ -1,0 +1,87 @@
+"""GPU parity for the version 2 extensions against the fp64 oracle: ragged
+draft-extend rows, tree verify, attention sinks, logit cap and the sliding-window
+pool slot translation.  Same tolerances as the topk = 1 parity tests."""
+
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decoding_verify_02_amd import workloads as W
+from test_verify_attn_gpu import DIMS, check, describe
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(dims, seed, **kw):
+    base = dict(batch=5, prefix_range=(0, 700), hq=16 if dims == 2 else 8,
+                hkv=1 if dims == 2 else 2, page_size=16, seed=seed)
+    base.update(kw)
+    return W.make_problem(name="ext", **base, **DIMS[dims])
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2, 3])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_ragged_rows(dims, splits):
+    check(_problem(dims, 700 + dims, ragged=True), num_splits=splits)
+
+
+def test_ragged_rows_explicit_counts_and_window():
+    p = _problem(0, 710, prefix_lens=[0, 1, 500, 37, 260], draft_counts=[1, 4, 2, 3, 1],
+                 window_left=40)
+    check(p)
+    check(p, num_splits=1)
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2, 3])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_tree_verify(dims, splits):
+    check(_problem(dims, 720 + dims, tree=True, poison=True), num_splits=splits)
+
+
+@pytest.mark.parametrize("draft", [1, 8])
+def test_tree_verify_draft_lengths(draft):
+    check(_problem(0, 730 + draft, tree=True, draft_len=draft, prefix_range=(0, 90)))
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2])
+def test_sinks(dims):
+    check(_problem(dims, 740 + dims, sinks=True))
+
+
+@pytest.mark.parametrize("dims", [0, 1, 2, 3])
+@pytest.mark.parametrize("cap", [0.5, 5.0])
+def test_logit_cap(dims, cap):
+    check(_problem(dims, 750 + dims, logit_cap=cap))
+
+
+@pytest.mark.parametrize("dims", [0, 2])
+def test_all_extensions_together(dims):
+    # ragged rows with sinks, a cap and a window; then a tree with sinks and a cap
+    check(_problem(dims, 760 + dims, ragged=True, sinks=True, logit_cap=3.0, window_left=100))
+    check(_problem(dims, 770 + dims, tree=True, sinks=True, logit_cap=3.0))
+
+
+def test_translate_slots_and_window_pool_table():
+    import torch
+    from speculative_decoding_verify_02_amd import binding as B
+
+    p = W.make_problem(name="swa", batch=4, prefix_range=(0, 400), hq=8, hkv=2, qk_dim=128,
+                       page_size=16, seed=780)
+    print(describe(p, label="translate"), flush=True)
+    rng = np.random.default_rng(780)
+    pmap = rng.permutation(p.num_pages + 7)[: p.num_pages]        # window pool is bigger
+    full_to_swa = (pmap[np.arange(p.num_slots) // 16] * 16 + np.arange(p.num_slots) % 16)
+    ref = oracle.translate_slots(p.kv_indices, full_to_swa)
+    dev = "cuda"
+    idx = torch.from_numpy(p.kv_indices.astype(np.int32)).to(dev)
+    mp = torch.from_numpy(full_to_swa.astype(np.int32)).to(dev)
+    got = B.verify_attn_translate_slots(idx, mp)
+    indptr = torch.from_numpy(p.kv_indptr.astype(np.int32)).to(dev)
+    bt, lens = B.verify_attn_build_block_table(indptr, got, 16, p.max_pages_per_seq)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+    bt_ref, lens_ref = oracle.block_table(p.kv_indptr, ref, 16, p.max_pages_per_seq)
+    assert np.array_equal(bt.cpu().numpy(), bt_ref)
+    assert np.array_equal(lens.cpu().numpy(), lens_ref)
+    # an empty list launches nothing
+    assert B.verify_attn_translate_slots(idx[:0], mp).numel() == 0
