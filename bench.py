@@ -94,7 +94,8 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int, workload: str,
     return out
 
 
-def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
+def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides=None,
+            label=None):
     import torch
 
     from speculative_decoding_verify_02_amd import binding
@@ -102,7 +103,9 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
     from speculative_decoding_verify_02_amd.runner import DeviceProblem
 
     t0 = time.time()
-    p = W.make_config(idx)
+    p = W.make_config(idx, **(overrides or {}))
+    if label:
+        p.name = label
     log(f"[bench] config {idx} {p.name}: inputs drawn in {time.time() - t0:.1f}s")
     kv_bytes = W.algorithmic_kv_bytes(p)
     fwd_bytes = kv_bytes  # the split-KV pass reads every visible key, draft keys included
@@ -156,6 +159,47 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print):
     return rec
 
 
+def time_translation(steps: int, log=print):
+    """verify_attn_translate_slots + the window pool's block table on the long-context
+    batch's token list, through a page-preserving full-to-window map."""
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verify_02_amd import binding
+    from speculative_decoding_verify_02_amd import workloads as W
+
+    p = W.make_config(2)
+    rng = np.random.default_rng(7)
+    pmap = rng.permutation(p.num_pages)
+    full_to_swa = (pmap[np.arange(p.num_slots) // p.page_size] * p.page_size
+                   + np.arange(p.num_slots) % p.page_size).astype(np.int32)
+    dev = "cuda"
+    idx = torch.from_numpy(p.kv_indices).to(dev)
+    mp = torch.from_numpy(full_to_swa).to(dev)
+    out = torch.empty_like(idx)
+    indptr = torch.from_numpy(p.kv_indptr).to(dev)
+    bt = torch.empty((p.batch, p.max_pages_per_seq), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        binding.verify_attn_translate_slots(idx, mp, out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for e in ev:
+        e[0].record(stream)
+        binding.verify_attn_translate_slots(idx, mp, out)
+        e[1].record(stream)
+        binding.verify_attn_build_block_table(indptr, out, p.page_size, p.max_pages_per_seq, bt)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    tr_us = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)[len(ev) // 2]
+    bt_us = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)[len(ev) // 2]
+    n = int(idx.numel())
+    log(f"[bench] slot translation: {n} slots in {tr_us:.1f} us, window-pool table {bt_us:.1f} us")
+    # bytes: read the slot, gather the map entry, write the result
+    return {"slots": n, "translate_us": round(tr_us, 2), "block_table_us": round(bt_us, 2),
+            "translate_gbs": round(12 * n / (tr_us * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(p, budget_s: float = 12.0, log=print):
     """The oracle as it stands on a bounded prefix of the workload's sequences, BLAS
     pinned to one thread (so `cores` is exactly what ran)."""
@@ -199,6 +243,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="headline workload index")
     ap.add_argument("--all-configs", action="store_true", help="also time the other large workloads")
+    ap.add_argument("--extensions", action="store_true",
+                    help="also time draft-extend rows, tree verify, sinks + logit cap and the "
+                         "window-pool slot translation")
     ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -235,6 +282,19 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    def summary(r):
+        return {
+            "us_per_step": round(r["ms_per_step"] * 1e3, 2), "fwd_us": round(r["fwd_us"], 2),
+            "combine_us": round(r["comb_us"], 2), "block_table_us": round(r["bt_us"], 2),
+            "kv_mb": round(r["kv_bytes"] / 1e6, 2),
+            "step_gbs": round(r["step_gbs"], 1), "fwd_gbs": round(r["fwd_gbs"], 1),
+            "fwd_pct_of_peak": round(100 * r["fwd_gbs"] / HBM_PEAK_GBS, 2),
+            "kernels_pct_of_peak": round(100 * r["kernels_gbs"] / HBM_PEAK_GBS, 2),
+            "call_us": r["call_us"],
+            "call_pct_of_peak": round(100 * r["kv_bytes"] / (r["call_us"]["median"] * 1e-6)
+                                      / 1e9 / HBM_PEAK_GBS, 2),
+            "splits": r["splits"], "kv_copies": r["copies"]}
+
     head = measure(args.config, args.steps, args.warmup, args.splits, log)
     per_config = {}
     if args.all_configs:
@@ -242,17 +302,18 @@ def main():
             if idx == args.config:
                 continue
             r = measure(idx, args.steps, args.warmup, None, log)
-            per_config[r["name"]] = {
-                "us_per_step": round(r["ms_per_step"] * 1e3, 2), "fwd_us": round(r["fwd_us"], 2),
-                "combine_us": round(r["comb_us"], 2), "block_table_us": round(r["bt_us"], 2),
-                "kv_mb": round(r["kv_bytes"] / 1e6, 2),
-                "step_gbs": round(r["step_gbs"], 1), "fwd_gbs": round(r["fwd_gbs"], 1),
-                "fwd_pct_of_peak": round(100 * r["fwd_gbs"] / HBM_PEAK_GBS, 2),
-                "kernels_pct_of_peak": round(100 * r["kernels_gbs"] / HBM_PEAK_GBS, 2),
-                "call_us": r["call_us"],
-                "call_pct_of_peak": round(100 * r["kv_bytes"] / (r["call_us"]["median"] * 1e-6)
-                                          / 1e9 / HBM_PEAK_GBS, 2),
-                "splits": r["splits"], "kv_copies": r["copies"]}
+            per_config[r["name"]] = summary(r)
+    extensions = {}
+    if args.extensions:
+        # the version 2 extensions on the long-context batch (and the MLA share)
+        for idx, over, label in (
+                (2, dict(ragged=True), "long-context-batch+draft-extend-rows"),
+                (2, dict(tree=True), "long-context-batch+tree-verify"),
+                (2, dict(sinks=True, logit_cap=30.0), "long-context-batch+sinks+logit-cap"),
+                (4, dict(tree=True), "mla-fp8-share+tree-verify")):
+            r = measure(idx, args.steps, args.warmup, None, log, overrides=over, label=label)
+            extensions[label] = summary(r)
+        extensions["window-pool-slot-translation"] = time_translation(args.steps, log)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 19     # bf16 elements
@@ -302,6 +363,8 @@ def main():
     }
     if per_config:
         out["per_config"] = per_config
+    if extensions:
+        out["extensions"] = extensions
     print(json.dumps(out), flush=True)
 
 

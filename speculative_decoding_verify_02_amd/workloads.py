@@ -358,5 +358,12 @@ def algorithmic_kv_bytes(p: Problem) -> int:
     page-rounding over-fetch.
     """
     per_tok = p.hkv * (p.qk_dim + (0 if p.v_aliases_k else p.v_dim)) * p.elem_bytes
-    toks = sum(visible_token_count(int(L), p.draft_len, p.window_left) for L in p.prefix_lens)
-    return int(toks) * per_tok
+    return int(sum(visible_token_count(int(L), n, p.window_left)
+                   for L, n in zip(p.prefix_lens, draft_rows(p)))) * per_tok
+
+
+def draft_rows(p: Problem):
+    """Draft rows (and draft keys) of each sequence: D, or qo_indptr's counts."""
+    if p.qo_indptr is None:
+        return [p.draft_len] * p.batch
+    return [int(p.qo_indptr[b + 1] - p.qo_indptr[b]) for b in range(p.batch)]
