@@ -2,37 +2,57 @@
 // qk_dim = 576 e4m3fn bytes, with V the first v_dim = 512 bytes of the same row
 // (PR #23146 review: qk_head_dim differs from v_head_dim; V is read from the K
 // cache view).  The dense M dimension is G*D <= 64 query rows (16 heads x 4 drafts
-// on one GPU's share), so each key costs ~140 kflop: the kernel keeps the MFMA
-// pipes fed from LDS while the cache streams in behind them.
+// on one GPU's share), so each key costs ~140 kflop and the kernel is built to keep
+// the matrix cores fed while the cache streams into LDS behind them.
 //
-//   workgroup = (KV head g, key range y: pieces of sequences), 4 waves; wave w owns
-//   rows 16w .. 16w+15 and keeps their q in registers for the whole piece.
-//   Tiles of 128 keys stream into a two-tile LDS ring with global_load_lds_dwordx4
-//   (one wave instruction copies one key's 576-byte row, 36 lanes x 16 bytes), so
-//   no registers hold data in flight: the next tile lands while this one computes.
-//   Page ids travel the same way (global_load_lds_dword), so the vector-memory
-//   counter covers everything a wave waits for and one vmcnt(0) per tile suffices.
-//   LDS rows sit at 592 t + 32 (t / 16) bytes: the 16 rows of an MFMA operand read
-//   and the 8 rows of a transposed read all fall on distinct banks.
-//   QK: S^T = K Q^T.  For d < 512 with v_mfma_f32_16x16x128_f8f6f4: K bytes as
-//       they are, and the bf16 q as two e4m3 terms hi + lo/16 (the lo product is
-//       scaled by 2^-4 through the MFMA's MX block scale), ~2^-9 relative error in
-//       q, the precision bf16 itself carries.  The rope tail d in [512, 576) uses
-//       v_mfma_f32_16x16x32_bf16 with K widened exactly to bf16 (every e4m3fn value
-//       is a bf16 value) and q in bf16.
-//   softmax: online, exp2 domain, row max across the 4 lanes of a row.  The
-//       reference max moves only when a score passes it by more than one (log2
-//       units), so p <= 2 and most tiles skip rescaling the accumulator.
-//   PV: O^T += V^T P^T with v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3).  P enters
-//       as two e4m3 terms, hi = e4m3(128 p) and lo = e4m3(16 (128 p - hi)) with the
-//       lo product scaled by 2^-4 through the MFMA's MX block scale: about 8
-//       significant bits per probability, close to bf16.  128 p <= 256 never
-//       overflows e4m3, and the factor keeps small probabilities out of the
-//       subnormal range; it is divided out at the end.  The running sum l uses the
-//       unrounded fp32 p.  The A operand (32 keys of one V column per lane) comes
-//       from four ds_read_b64_tr_b8 transposed LDS reads: in each 16-lane group,
-//       lanes 2k and 2k+1 address the two 8-byte halves of a 16-column slice of key
-//       row k, and lane c receives column c of the 8 rows.
+//   workgroup = (KV head g, key range y: pieces of sequences), 8 waves, two per
+//   SIMD.  Wave w = (row group rg = w % 4, half hf = w / 4): the pair (rg, 0),
+//   (rg, 1) shares query rows 16 rg .. 16 rg + 15, whose q both keep in registers.
+//   Per tile of 128 keys:
+//     QK  wave hf scores keys 64 hf .. 64 hf + 63 of the tile (S^T = K Q^T);
+//     the pair swaps row maxima through LDS, so both take the same running max,
+//     then swaps its probabilities (two e4m3 bytes each), so both hold P for all
+//     128 keys;
+//     PV  wave hf accumulates output columns 256 hf .. 256 hf + 255 over all 128
+//     keys (O^T += V^T P^T).
+//   Two waves per SIMD let one wave's softmax, exchanges and waits run under the
+//   other's matrix instructions; each wave holds 16 rows x 256 fp32 columns.
+//
+// Memory: the 512 latent bytes of each key stream into a two-tile LDS ring with
+// global_load_lds_dwordx4, one 64-lane instruction per two keys (1 KB), so no
+// registers hold data in flight.  A wave's 8 copies of the next tile are spread over
+// its QK phase, so a copy that waits for room in the memory queue stalls the wave
+// between matrix instructions rather than before them.  The 64 rope bytes, read only
+// by QK, go to a single rope buffer that is refilled for the next tile once every
+// wave has passed the max exchange.  One vmcnt(0) per tile is the only wait for
+// copies; the copies are inline assembly, so the compiler adds none of its own, and
+// every compiler-visible load of a tile is issued before its copies.
+//   Latent row t sits at 512 t with 16-byte chunk c stored at chunk c ^ f(t),
+//   f(t) = (t % 16) ^ 8 ((t / 16) % 2): the 16 rows of an operand read and the 16
+//   rows {0..7, 16..23} (or {8..15, 24..31}) of a transposed read fall on distinct
+//   banks.  Rope row t sits at 64 t with chunk c stored at c ^ ((t / 4) % 4).
+//
+//   QK: for d < 512 v_mfma_scale_f32_16x16x128_f8f6f4 with the K bytes as they are
+//       and the bf16 q as two e4m3 terms hi + lo/16 (the lo product is scaled by
+//       2^-4 through the MFMA's MX block scale), ~2^-9 relative error in q, the
+//       precision bf16 itself carries.  The rope tail d in [512, 576) uses
+//       v_mfma_f32_16x16x32_bf16 with K widened exactly to bf16 (every e4m3fn
+//       value is a bf16 value) and q in bf16.
+//   softmax: online, exp2 domain.  The running max moves only when a score passes
+//       it by more than one (log2 units), so p <= 2 and most tiles skip rescaling
+//       the accumulator.
+//   PV: v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3 x e4m3).  P enters as two e4m3
+//       terms, hi = e4m3(128 p) and lo = e4m3(16 (128 p - hi)), the lo product
+//       scaled by 2^-4 through the MX block scale: about 8 significant bits per
+//       probability.  128 p <= 256 never overflows e4m3, and the factor keeps small
+//       probabilities out of the subnormal range; it is divided out at the end.
+//       The running sum uses the unrounded fp32 p.  The A operand (32 keys of one V
+//       column per lane) comes from four ds_read_b64_tr_b8 transposed LDS reads: in
+//       each 16-lane group, lanes 2k and 2k+1 address the two 8-byte halves of a
+//       16-column slice of key row k, and lane c receives column c of the 8 rows.
+//       The 32 keys of lane group j are, in order, the wave's own 16 keys
+//       64 hf + 16 s + 4 j + i and then its partner's (s, i < 4): exactly the
+//       scores the lane and its partner lane hold, so P needs no reshuffling.
 
 #include <limits.h>
 #include <math.h>
@@ -44,12 +64,13 @@ namespace va {
 namespace {
 
 constexpr int kMB = 128;              // keys per tile
-constexpr int kKRB = 576;             // K row bytes
-constexpr int kVRB = 512;             // V bytes per row (first part of the K row)
-constexpr int kRS = kKRB + 16;        // LDS row stride
-constexpr int kTileBytes = 76032;     // row_off(127) + 576, rounded up to 128
-constexpr int kCT = kVRB / 16;        // O^T column tiles
-constexpr int kKPW = kMB / kWaves;    // keys each wave copies per tile
+constexpr int kLat = 512;             // latent bytes per key (= V)
+constexpr int kRope = 64;             // rope bytes per key
+constexpr int kNW = 8;                // waves per workgroup
+constexpr int kKPW = kMB / kNW;       // keys each wave copies per tile
+constexpr int kLatTile = kMB * kLat;
+constexpr int kRopeTile = kMB * kRope;
+constexpr int kCT = 256 / 16;         // O^T column tiles per wave
 constexpr float kPScale = 128.f;      // P scale for e4m3 (p <= 2^kLazy, so 128 p <= 256 < 448)
 constexpr float kLazy = 1.f;          // log2 headroom before the running max is moved
 constexpr int kE8M0One = 127;         // MX block scale exponents (bias 127)
@@ -59,14 +80,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(8 * sizeof(uint32_t)))) uint32_t u32x8;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-// Byte offset of key row t inside a tile.  The 16-byte slot of row t mod 16 is
-// 5 t + 2 (t / 16): distinct for the 16 consecutive rows of an operand read and for
-// the rows {4j + i, 16 + 4j + i} (i < 4) a transposed read takes together.
-__device__ __forceinline__ int row_off(int t) { return t * kRS + (t >> 4) * 32; }
-static_assert(127 * kRS + 7 * 32 + kKRB <= kTileBytes, "tile holds 128 rows");
+// Chunk permutation of latent row t (16-byte chunks, XOR inside aligned groups of 16).
+__device__ __forceinline__ int lat_swz(int t) { return (t & 15) ^ (((t >> 4) & 1) << 3); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -84,7 +103,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Copies to LDS at `lds` + lane * size straight from global memory.  Inline assembly,
+// Copies to LDS at `lds` + lane * 16 straight from global memory.  Inline assembly,
 // so the compiler (which does not see these copies) adds no waits of its own before
 // LDS reads; the waits are explicit.  M0 holds the wave's LDS base and needs one
 // wait state before the copy reads it.
@@ -92,43 +111,71 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds) : "memory", "m0");
 }
-// Same with a wave-uniform base in SGPRs and a per-lane 32-bit byte offset.
-__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
-}
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Token of score slot i (0..31) of lane group j: tile i/4, accumulator row 4j + i%4.
-__device__ __forceinline__ int slot_token(int j, int i) { return 16 * (i >> 2) + 4 * j + (i & 3); }
+// Workgroup barrier ordering LDS only: outstanding copies into the ring stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
-// LDS of the one workgroup a compute unit holds: the two-tile ring and each wave's
-// page ids for its keys of the next two tiles.
-__shared__ __attribute__((aligned(128))) uint8_t s_ring[2][kTileBytes];
-__shared__ __attribute__((aligned(16))) int32_t s_pid[2][kWaves][kKPW];
+// LDS of the one workgroup a compute unit holds: the two-tile latent ring, the rope
+// buffer, and the pair exchanges (probabilities: [wave][hi, lo][lane][16 bytes];
+// row maxima and sums: [wave][row]).
+__shared__ __attribute__((aligned(128))) uint8_t s_lat[2][kLatTile];
+__shared__ __attribute__((aligned(128))) uint8_t s_rope[kRopeTile];
+__shared__ __attribute__((aligned(16))) i32x4 s_xp[kNW][2][64];
+__shared__ float s_xm[kNW][16];
 
 }  // namespace
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-void splitkv_mla_fp8_kernel(FwdParams P) {
+__global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3;
+  const int hf = wave >> 2;
+  const int partner = wave ^ 4;
   const int n = lane & 15;
   const int j = lane >> 4;
   const int g = blockIdx.x;
   PieceWalk pw;
   if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
 
-  const int row = wave * 16 + n;
+  const int row = rg * 16 + n;
   const bool tree = P.draft_slots != nullptr;
   const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
+
+  // per-lane LDS offsets, fixed for the kernel:
+  //   qoff[e][x]: 16-byte half e of the lane's 32-byte K operand slice (row 64 hf + n,
+  //            chunks 8 kb + 2 j + e) for token tile tt and k-block kb with
+  //            x = (kb ^ tt) % 2; the rest (8192 tt + 256 (kb / 2)) is an immediate;
+  //   voff[r]: transposed V read of key slots 8r .. 8r+7 (own keys first), this
+  //            wave's columns, the lane's 8-byte half; column tile ct reads at
+  //            voff[r] ^ 16 ct (bits 4..7 of voff hold the row's permutation);
+  //   roff[h]: rope k-step h of token tile 0 (lane group j: 8 bytes at 32 h + 8 j);
+  //   cx:      the lane's source chunk for copy pair 0 (pair i: cx ^ 2 i).
+  int qoff[2][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      qoff[e][x] = kLat * (64 * hf + n) + 16 * ((2 * j + e) ^ (n & 7)) + 128 * ((n >> 3) ^ x);
+  int voff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k8 = n >> 1;
+    const int t = 64 * (hf ^ (r >> 1)) + 16 * (2 * (r & 1) + (k8 >> 2)) + 4 * j + (k8 & 3);
+    voff[r] = kLat * t + 256 * hf + 8 * (n & 1) + 16 * lat_swz(t);
+  }
+  const int cx = (lane & 31) ^ (lane >> 5) ^ ((wave & 1) << 3);
+  int roff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    roff[h] = (64 * hf + n) * kRope + 16 * ((2 * h + (j >> 1)) ^ ((n >> 2) & 3)) + 8 * (j & 1);
 
   do {
   const Piece pc = pw.piece(P);
@@ -142,63 +189,110 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
   // the lane's row: draft row_i of sequence b (rows past the sequence's count idle)
   const bool rv = row < P.rows && row / P.group < seq_rows(P, b);
   const int row_i = rv ? row / P.group : 0;
-
-  // page ids of this wave's keys of tile k -> s_pid[k % 2][wave]: entry e is the
-  // page of the wave's first key plus e, clamped to the table row
-  auto copy_pids = [&](int k) {
-    const int tw = min(t_begin + k * kMB + wave * kKPW, t_last);
-    const int e = min((tw >> lg) + lane, P.max_pages - 1);
-    if (lane < kKPW) dma4(bt_row + e, lds_addr(&s_pid[k & 1][wave][0]));
-  };
-  // this wave's keys of tile k -> ring buffer k % 2 (one key row per instruction).
-  // Lane l < 32 looks up the slot of key l with one LDS read; each copy then takes
-  // its key's slot from that lane into a scalar base address.
-  auto copy_tile = [&](int k) {
-    const int t0 = t_begin + k * kMB + wave * kKPW;
-    const int pbase = min(t0, t_last) >> lg;
-    uint8_t* ring = s_ring[k & 1];
-    const int tl = min(t0 + (lane & (kKPW - 1)), t_last);
-    int slot_l = (s_pid[k & 1][wave][(tl >> lg) - pbase] << lg) | (tl & pmask);
-    if (tree && t0 + kKPW - 1 >= L)   // tree verify: draft keys at their own slots
-      slot_l = tl >= L ? P.draft_slots[b * P.draft + (tl - L)] : slot_l;
+  // (row bounds and tree bits are loaded before any copy is issued, so the
+  // compiler's waits for them never count copies in flight)
+  // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
+  const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
+  const int row_hi = rv ? (tree ? t_last : min(t_last, L + row_i)) : -1;
+  const uint32_t tbits = (tree && rv) ? tree_bits(P, b, row_i) : 0u;
+  // keys every row of the pair sees: key halves inside [wave_lo, wave_hi] need no
+  // masking (tree draft keys and capped logits always take the general path)
+  int wave_lo = rv ? row_lo : INT_MIN;
+  int wave_hi = rv ? (tree ? min(row_hi, L - 1) : row_hi) : INT_MAX;
+  if (P.logit_cap > 0.f) wave_hi = INT_MIN;
 #pragma unroll
-    for (int u = 0; u < kKPW; ++u) {
-      const int slot = __builtin_amdgcn_readlane(slot_l, u);
-      if (lane < kKRB / 16)
-        dma16_s(kg + (int64_t)slot * P.k_sslot, 16 * lane, lds_addr(ring + row_off(wave * kKPW + u)));
-    }
+  for (int off = 1; off < 16; off <<= 1) {
+    wave_lo = max(wave_lo, __shfl_xor(wave_lo, off, 64));
+    wave_hi = min(wave_hi, __shfl_xor(wave_hi, off, 64));
+  }
+  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
+
+  // key of lane l < 16 among this wave's 16 copies of tile k (clamped to the piece)
+  auto copy_key = [&](int k) { return min(t_begin + k * kMB + wave * kKPW + (lane & 15), t_last); };
+  auto load_pid = [&](int k) -> int {
+    const int t = copy_key(k);
+    return (tree && t >= L) ? 0 : bt_row[t >> lg];
+  };
+  // The slot may come from a load (tree verify): the empty asm consumes it here, so
+  // the compiler's wait for that load sits before the copies, never after them.
+  auto make_slot = [&](int pid, int k) -> int {
+    const int t = copy_key(k);
+    int slot = (tree && t >= L) ? P.draft_slots[b * P.draft + (t - L)]  // tree verify draft keys
+                                : (pid << lg) | (t & pmask);
+    asm volatile("" : "+v"(slot));
+    return slot;
+  };
+  // latent bytes of keys 2i, 2i+1 of this wave's 16 keys of tile k -> ring buffer
+  // k % 2, one instruction: lanes 0..31 copy the first key's row, lanes 32..63 the
+  // second's, lane l into chunk position l % 32 (which holds chunk (l % 32) ^ f(t))
+  auto copy_pair = [&](int k, int slot_l, int i) {
+    const int s0 = __builtin_amdgcn_readlane(slot_l, 2 * i);
+    const int s1 = __builtin_amdgcn_readlane(slot_l, 2 * i + 1);
+    int slot = lane < 32 ? s0 : s1;
+    // ordered after the previous copy, so the address math is not hoisted (and held
+    // in registers) ahead of it
+    asm volatile("" : "+v"(slot));
+    dma16(kg + (int64_t)slot * P.k_sslot + 16 * (cx ^ (2 * i)),
+          lds_addr(s_lat[k & 1] + (wave * kKPW + 2 * i) * kLat));
+  };
+  // rope bytes of this wave's keys -> rope buffer, one instruction: lane l copies
+  // chunk l % 4 position of key l / 4 (chunks permuted per row against bank conflicts)
+  auto copy_rope = [&](int slot_l) {
+    const int u = lane >> 2;
+    const int s = __shfl(slot_l, u, 64);
+    const int c = (lane & 3) ^ ((u >> 2) & 3);
+    dma16(kg + (int64_t)s * P.k_sslot + kLat + 16 * c, lds_addr(s_rope + wave * kKPW * kRope));
   };
 
-  copy_pids(0);
-  if (ntile > 1) copy_pids(1);
-  wait_copies();
-  copy_tile(0);
-
-  // this wave's 16 q rows in registers: for d < 512 as two e4m3 terms (hi = e4m3(q),
+  int pid = 0, slot_nx = 0;
+  // this pair's 16 q rows in registers: for d < 512 as two e4m3 terms (hi = e4m3(q),
   // lo = e4m3(16 (q - hi)), together ~2^-9 relative error, the precision of the
   // bf16 q itself), the 64-wide rope tail d >= 512 as bf16.  Lane group j holds
   // elements 128kb + 32j + [0, 32) (and 512 + 32h + 8j + [0, 8) of the tail), the
   // k-slots of the K operand read below.
-  i32x8 qh[kVRB / 128], ql[kVRB / 128];
+  // The loads (q, page ids of tiles 0 and 1) are issued before the copies of tile 0,
+  // and q is converted while those copies are in flight.
+  i32x8 qh[kLat / 128], ql[kLat / 128];
   u32x4 qr[2];
   {
     const int hh = rv ? row % P.group : 0;
     const uint8_t* qp =
         P.q + (int64_t)(seq_row0(P, b) + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
+    u32x4 raw[kLat / 128][4];
 #pragma unroll
-    for (int kb = 0; kb < kVRB / 128; ++kb) {
-      u32x4 raw[4];
+    for (int kb = 0; kb < kLat / 128; ++kb)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        raw[c] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (128 * kb + 32 * j + 8 * c))
-                    : u32x4{0u, 0u, 0u, 0u};
+        raw[kb][c] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (128 * kb + 32 * j + 8 * c))
+                        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      qr[h] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (kLat + 32 * h + 8 * j))
+                 : u32x4{0u, 0u, 0u, 0u};
+    int pid0 = load_pid(0);
+    if (ntile > 1) pid = load_pid(1);
+    slot_nx = make_slot(pid0, 0);
+    // q has landed (it was loaded before the page ids); the empty asm makes the
+    // compiler take that wait here, not after the copies
+#pragma unroll
+    for (int kb = 0; kb < kLat / 128; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(raw[kb][c]));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(qr[h]));
+#pragma unroll
+    for (int i = 0; i < kKPW / 2; ++i) copy_pair(0, slot_nx, i);
+    copy_rope(slot_nx);
+#pragma unroll
+    for (int kb = 0; kb < kLat / 128; ++kb) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float x[8];  // q elements, saturated to the e4m3 range (+-448)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = fminf(fmaxf(__uint_as_float(raw[c][e] << 16), -448.f), 448.f);
-          x[2 * e + 1] = fminf(fmaxf(__uint_as_float(raw[c][e] & 0xffff0000u), -448.f), 448.f);
+          x[2 * e] = fminf(fmaxf(__uint_as_float(raw[kb][c][e] << 16), -448.f), 448.f);
+          x[2 * e + 1] = fminf(fmaxf(__uint_as_float(raw[kb][c][e] & 0xffff0000u), -448.f), 448.f);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -215,27 +309,7 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
         }
       }
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      qr[h] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (kVRB + 32 * h + 8 * j))
-                 : u32x4{0u, 0u, 0u, 0u};
   }
-  // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
-  const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
-  const int row_hi = rv ? (tree ? t_last : min(t_last, L + row_i)) : -1;
-  const uint32_t tbits = (tree && rv) ? tree_bits(P, b, row_i) : 0u;
-  // keys every row of the wave sees: tiles inside [wave_lo, wave_hi] need no masking
-  // (tree draft keys and capped logits always take the general path)
-  int wave_lo = rv ? row_lo : INT_MIN;
-  int wave_hi = rv ? (tree ? min(row_hi, L - 1) : row_hi) : INT_MAX;
-  if (P.logit_cap > 0.f) wave_hi = INT_MIN;
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    wave_lo = max(wave_lo, __shfl_xor(wave_lo, off, 64));
-    wave_hi = min(wave_hi, __shfl_xor(wave_hi, off, 64));
-  }
-  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
-  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[kCT];
@@ -244,31 +318,36 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
 
   for (int k = 0; k < ntile; ++k) {
     // this wave's copies of tile k (and page ids of tile k + 1) have landed; the
-    // barrier shows every wave's and frees the buffer tile k - 1 was computed from
+    // barrier shows every wave's and frees the ring buffer tile k - 1 was read from
     wait_copies();
-    __syncthreads();
-    if (k + 1 < ntile) copy_tile(k + 1);
-    if (k + 2 < ntile) copy_pids(k + 2);
+    lds_barrier();
+    // compiler-visible loads go before the copies: a wait the compiler places for
+    // them then never counts the copies still in flight
+    const bool next = k + 1 < ntile;
+    if (next) slot_nx = make_slot(pid, k + 1);
+    if (k + 2 < ntile) pid = load_pid(k + 2);
 
     const int t0 = t_begin + k * kMB;
-    const uint8_t* tile = s_ring[k & 1];
+    const int th = t0 + 64 * hf;  // first key this wave scores
+    const uint8_t* lat = s_lat[k & 1];
 
-    // a4: S^T for 8 token tiles
-    f32x4 sacc[8];
+    // a4: S^T for the wave's 4 token tiles of 16 keys
+    f32x4 sacc[4];
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 4; ++tt) sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     // d < 512: fp8 x fp8 (K bytes as they are, q as hi + lo terms).  Token tiles go
     // in pairs so the two products into one accumulator are not back to back.
 #pragma unroll
-    for (int kb = 0; kb < kVRB / 128; ++kb) {
+    for (int kb = 0; kb < kLat / 128; ++kb) {
 #pragma unroll
-      for (int tt = 0; tt < 8; tt += 2) {
+      for (int tt = 0; tt < 4; tt += 2) {
         i32x8 ka[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const uint8_t* kp = tile + row_off(16 * (tt + e) + n) + 128 * kb + 32 * j;
-          const u32x4 k0 = *reinterpret_cast<const u32x4*>(kp);
-          const u32x4 k1 = *reinterpret_cast<const u32x4*>(kp + 16);
+          const int x = (kb ^ (tt + e)) & 1;
+          const int imm = 8192 * (tt + e) + 256 * (kb >> 1);
+          const u32x4 k0 = *reinterpret_cast<const u32x4*>(lat + qoff[0][x] + imm);
+          const u32x4 k1 = *reinterpret_cast<const u32x4*>(lat + qoff[1][x] + imm);
           ka[e] = __builtin_bit_cast(i32x8, u32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
         }
 #pragma unroll
@@ -278,88 +357,101 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
         for (int e = 0; e < 2; ++e)
           sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], ql[kb], sacc[tt + e], 0, 0, 0,
                                                                           kE8M0One, 0, kE8M0Sixteenth);
+        // one copy of the next tile per operand group (8 per tile)
+        if (next) copy_pair(k + 1, slot_nx, kb * 2 + tt / 2);
       }
     }
     // rope tail d in [512, 576): bf16 k-steps, lane group j holds 512 + 32h + 8j + [0, 8)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const u32x2 kr = *reinterpret_cast<const u32x2*>(tile + row_off(16 * tt + n) + kVRB + 32 * h + 8 * j);
+      for (int tt = 0; tt < 4; ++tt) {
+        const u32x2 kr = *reinterpret_cast<const u32x2*>(s_rope + roff[h] + 16 * kRope * tt);
         const u32x2 w0 = fp8x4_to_bf16x4(kr[0]), w1 = fp8x4_to_bf16x4(kr[1]);
         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]}), as_bf16x8(qr[h]), sacc[tt], 0, 0, 0);
       }
     }
 
-    // online softmax over the lane's 32 scores (row n)
-    float sc[32];
+    // the lane's 16 scores of row n: slot e is key th + 16 (e / 4) + 4 j + e % 4
+    float sc[16];
     float bmax = -INFINITY;
-    if (t0 >= wave_lo && t0 + kMB - 1 <= wave_hi) {
+    if (th >= wave_lo && th + 63 <= wave_hi) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
+      for (int e = 0; e < 16; ++e) {
         sc[e] = sacc[e >> 2][e & 3] * P.c_log2;
         bmax = fmaxf(bmax, sc[e]);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int t = t0 + slot_token(j, e);
+      for (int e = 0; e < 16; ++e) {
+        const int t = th + 16 * (e >> 2) + 4 * j + (e & 3);
         const bool ok = key_ok(t, row_lo, row_hi, L, tbits, tree);
         sc[e] = ok ? sacc[e >> 2][e & 3] * P.c_log2 : -INFINITY;
       }
       if (P.logit_cap > 0.f) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) sc[e] = sc[e] == -INFINITY ? sc[e] : cap_log2(sc[e], P.logit_cap);
+        for (int e = 0; e < 16; ++e) sc[e] = sc[e] == -INFINITY ? sc[e] : cap_log2(sc[e], P.logit_cap);
       }
 #pragma unroll
-      for (int e = 0; e < 32; ++e) bmax = fmaxf(bmax, sc[e]);
+      for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, sc[e]);
     }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    if (j == 0) s_xm[wave][n] = bmax;
+    // every wave's maxima are written and every rope read of tile k is done
+    lds_barrier();
+    if (next) copy_rope(slot_nx);
+    bmax = fmaxf(bmax, s_xm[partner][n]);
+
     // the reference max moves only when a score passes it by more than kLazy, so
-    // most tiles leave the accumulator alone; p = 2^(s - m) stays <= 2^kLazy
+    // most tiles leave the accumulator alone; p = 2^(s - m) stays <= 2^kLazy.  Both
+    // waves of the pair take the same decision from the same maxima.
     const bool grow = bmax > m_run + kLazy;
     const float m_new = grow ? bmax : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    for (int e = 0; e < 16; ++e) {
       sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
       psum += sc[e];
     }
-    // the accumulator lives in AGPRs: rescale only when some row with a nonzero
-    // accumulator moved its max
-    if (__any(grow && m_run != -INFINITY)) {
-#pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) oacc[ct] *= alpha;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
     // P in two e4m3 terms: hi = e4m3(128 p), lo = e4m3(16 (128 p - hi)); the lo
-    // product enters the same accumulator through the MFMA's B scale 2^-4.  The
-    // pair keeps about 8 significant bits of each probability.
-    i32x8 pb, pl;
+    // product enters the same accumulator through the MFMA's B scale 2^-4
+    i32x4 ph, pl;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    for (int d = 0; d < 4; ++d) {
       const float x0 = sc[4 * d] * kPScale, x1 = sc[4 * d + 1] * kPScale;
       const float x2 = sc[4 * d + 2] * kPScale, x3 = sc[4 * d + 3] * kPScale;
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-      pb[d] = w;
+      ph[d] = w;
       const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
       const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
       int wl = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h01[0]) * 16.f, (x1 - h01[1]) * 16.f, 0, false);
       wl = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - h23[0]) * 16.f, (x3 - h23[1]) * 16.f, wl, true);
       pl[d] = wl;
     }
+    s_xp[wave][0][lane] = ph;
+    s_xp[wave][1][lane] = pl;
+    // the pair's probabilities are written
+    lds_barrier();
+    const i32x4 qph = s_xp[partner][0][lane];
+    const i32x4 qpl = s_xp[partner][1][lane];
+    const i32x8 pb = i32x8{ph[0], ph[1], ph[2], ph[3], qph[0], qph[1], qph[2], qph[3]};
+    const i32x8 pb_lo = i32x8{pl[0], pl[1], pl[2], pl[3], qpl[0], qpl[1], qpl[2], qpl[3]};
 
-    // a5: O^T += V^T P^T, V^T via transposed LDS reads (tokens of slots 8r..8r+7)
-    __attribute__((address_space(3))) char* lbase = (__attribute__((address_space(3))) char*)tile;
-    int voff[4];
+    // rescale only when some row with a nonzero accumulator moved its max
+    if (__any(grow && m_run != -INFINITY)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) voff[r] = row_off(slot_token(j, 8 * r + (n >> 1))) + 8 * (n & 1);
+      for (int ct = 0; ct < kCT; ++ct) oacc[ct] *= alpha;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // a5: O^T += V^T P^T over all 128 keys, this wave's 256 columns
+    __attribute__((address_space(3))) char* lbase = (__attribute__((address_space(3))) char*)lat;
 #pragma unroll
     for (int ct = 0; ct < kCT; ct += 2) {
       i32x8 a[2];
@@ -368,7 +460,7 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              reinterpret_cast<lds_i32x2*>(lbase + voff[r] + 16 * (ct + e)));
+              reinterpret_cast<lds_i32x2*>(lbase + (voff[r] ^ (16 * (ct + e)))));
           a[e][2 * r] = x[0];
           a[e][2 * r + 1] = x[1];
         }
@@ -378,18 +470,21 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
         oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pb, oacc[ct + e], 0, 0, 0, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pl, oacc[ct + e], 0, 0, 0,
+        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pb_lo, oacc[ct + e], 0, 0, 0,
                                                                         kE8M0One, 0, kE8M0Sixteenth);
     }
   }
 
-  // each lane summed only its own tokens: total the 4 lanes of the row
+  // each lane summed only its own keys: total the 4 lanes of the row, then the pair
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+  if (j == 0) s_xm[wave][n] = l_run;
+  lds_barrier();
+  l_run += s_xm[partner][n];
   if (rv) {
     const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
     const float inv = l_run > 0.f ? P.v_scale / (l_run * kPScale) : 0.f;
-    float* po = P.part_o + (split_id * P.rows + row) * kVRB + 4 * j;
+    float* po = P.part_o + (split_id * P.rows + row) * kLat + 256 * hf + 4 * j;
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
       f32x4 o = oacc[ct];
@@ -397,16 +492,18 @@ void splitkv_mla_fp8_kernel(FwdParams P) {
       for (int r = 0; r < 4; ++r) o[r] *= inv;
       *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
     }
-    if (j == 0)
+    if (hf == 0 && j == 0)
       P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
-  __syncthreads();  // every wave is done with the ring before the next piece refills it
+  // every wave is done with the ring, the rope buffer and the exchanges before the
+  // next piece refills them
+  lds_barrier();
   } while (pw.next(P));
 }
 
 int launch_splitkv_mla_fp8(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t st) {
   if (p.rows > 64) return VA_EUNSUPPORTED;
-  return launch_kernel(reinterpret_cast<const void*>(&splitkv_mla_fp8_kernel), grid, dim3(256),
+  return launch_kernel(reinterpret_cast<const void*>(&splitkv_mla_fp8_kernel), grid, dim3(kNW * 64),
                        fp, st);
 }
 
