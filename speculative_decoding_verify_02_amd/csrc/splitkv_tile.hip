@@ -6,9 +6,11 @@
 // contiguous elements.  A workgroup therefore takes HPC KV heads of one
 // key range (pieces of sequences) and loads each 16-token block cooperatively: every load
 // instruction reads whole runs of a slot row (all HPC heads), so HBM sees long
-// contiguous reads instead of one head's 256-byte slices.  K and V blocks go to
-// double-buffered LDS tiles (the next block loads while this one computes);
-// each wave then reads only its own head's slice:
+// contiguous reads instead of one head's 256-byte slices.  Three blocks are in
+// flight in registers ahead of the one being computed (the loop is unrolled by
+// three so each register set has a fixed name), and each is staged into one of
+// two LDS tiles (K and V) one block before it is computed; each wave then reads
+// only its own head's slice:
 //   QK: A operand = K rows from LDS (ds_read_b128), B = the wave's Q^T rows held
 //       in registers, v_mfma_f32_16x16x32_bf16 -> S^T (16 tokens x 16 rows);
 //   softmax: online, exp2 domain, row max across the 4 lanes of a row;
@@ -22,6 +24,8 @@
 
 #include <limits.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "va_internal.h"
 
@@ -51,8 +55,11 @@ struct TileGeo {
 
 }  // namespace
 
+constexpr int kDepth = 3;  // blocks in flight in registers
+
 template <int D, int HPC, int NRG>
-__global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams P) {
+__global__ __launch_bounds__(64 * HPC * NRG) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void splitkv_tile_kernel(FwdParams P) {
   using G = TileGeo<D, HPC, NRG>;
   constexpr int KS = D / 32;   // QK k-steps
   constexpr int CT = D / 16;   // O^T column tiles
@@ -113,38 +120,61 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
   // this thread's load chunks: q = 64*W*u + tid -> token q / CH, head (q % CH) / (RB/16)
-  auto lane_slot = [&](int t0) {
-    return key_slot(P, bt_row, b, L, min(t0 + (lane & (kTB - 1)), t_last), lg, pmask);
+  // A slot lookup in two parts: lane_raw loads the page id of the lane's token of the
+  // block at t0 (its draft slot for tree-verify draft keys) with no branch, and
+  // lane_slot turns it into the slot where the value is used, so the wait for the
+  // load sits at the use.
+  auto lane_raw = [&](int t0) -> int {
+    const int t = min(t0 + (lane & (kTB - 1)), t_last);
+    const int32_t* src = (tree && t >= L) ? P.draft_slots + b * P.draft + (t - L) : bt_row + (t >> lg);
+    return *src;
   };
-  // one register set holds the next block while this one computes
-  u32x4 kr[G::NLD], vr[G::NLD];
-  auto load = [&](int sl_lane) {
+  auto lane_slot = [&](int raw, int t0) -> int {
+    const int t = min(t0 + (lane & (kTB - 1)), t_last);
+    return (tree && t >= L) ? raw : (raw << lg) | (t & pmask);
+  };
+  // kDepth register sets: set s holds the blocks b with b % kDepth == s
+  u32x4 kr[kDepth][G::NLD], vr[kDepth][G::NLD];
+  auto load = [&](auto set, int sl_lane) {
 #pragma unroll
     for (int u = 0; u < G::NLD; ++u) {
       const int q = 64 * G::W * u + tid;
       const int tok = q / G::CH, c = q % G::CH;
       const int hd = c / (G::RB / 16), cc = c % (G::RB / 16);
       const int64_t slot = __shfl(sl_lane, tok, 64);
-      kr[u] = *reinterpret_cast<const u32x4*>(P.k + slot * P.k_sslot + (int64_t)(g0 + hd) * P.k_shead + 16 * cc);
-      vr[u] = *reinterpret_cast<const u32x4*>(P.v + slot * P.v_sslot + (int64_t)(g0 + hd) * P.v_shead + 16 * cc);
+      kr[set][u] = *reinterpret_cast<const u32x4*>(P.k + slot * P.k_sslot + (int64_t)(g0 + hd) * P.k_shead + 16 * cc);
+      vr[set][u] = *reinterpret_cast<const u32x4*>(P.v + slot * P.v_sslot + (int64_t)(g0 + hd) * P.v_shead + 16 * cc);
     }
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](auto set, int buf) {
 #pragma unroll
     for (int u = 0; u < G::NLD; ++u) {
       const int q = 64 * G::W * u + tid;
       const int off = (q / G::CH) * G::RS + 16 * (q % G::CH);
-      *reinterpret_cast<u32x4*>(&kt[buf][off]) = kr[u];
-      *reinterpret_cast<u32x4*>(&vt[buf][off]) = vr[u];
+      *reinterpret_cast<u32x4*>(&kt[buf][off]) = kr[set][u];
+      *reinterpret_cast<u32x4*>(&vt[buf][off]) = vr[set][u];
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(kDepth == 3, "the loop below is unrolled by three");
 
-  int sl_next = 0;
+  // Page ids: at step b (set s = b % kDepth), pid[s] holds block b + kDepth's and is
+  // refilled with block b + 2 kDepth's once used.  A lookup is issued kDepth steps
+  // before its use and each register is written and read once per kDepth steps, so
+  // the compiler's wait for a lookup leaves the later steps' data loads in flight.
+  int pid[kDepth] = {0, 0, 0};
   {
-    const int sl0 = lane_slot(t_begin);
-    if (nblk > 1) sl_next = lane_slot(t_begin + kTB);
-    load(sl0);
-    stage(0);
+    const int s0 = lane_raw(t_begin);
+    const int s1 = lane_raw(t_begin + kTB);
+    const int s2 = lane_raw(t_begin + 2 * kTB);
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) pid[u] = lane_raw(t_begin + (kDepth + u) * kTB);
+    load(S0{}, lane_slot(s0, t_begin));
+    load(S1{}, lane_slot(s1, t_begin + kTB));
+    load(S2{}, lane_slot(s2, t_begin + 2 * kTB));
+    stage(S0{}, 0);
   }
   __syncthreads();
 
@@ -153,21 +183,33 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
   // columns starting at 4*(n%4) of each 16-column tile
   const int vlane = (4 * j + (n >> 2)) * G::RS + hoff + 8 * (n & 3);
 
-  for (int blk = 0; blk < nblk; ++blk) {
+  // One block: its set refills with block blk + kDepth, the block is computed from
+  // LDS, and block blk + 1 is staged into the other LDS tile.  Steps have no
+  // branches, so the compiler keeps exact counts of the loads in flight: blocks past
+  // the piece load its last token (a valid address) and are computed with every key
+  // masked, which leaves the softmax state unchanged.
+  auto step = [&](auto set, int blk) {
     const int buf = blk & 1;
     const int t0 = t_begin + blk * kTB;
-    if (blk + 1 < nblk) {
-      load(sl_next);  // next block in flight during this block's math
-      if (blk + 2 < nblk) sl_next = lane_slot(t0 + 2 * kTB);
-    }
+    constexpr int si = decltype(set)::value;
+    load(set, lane_slot(pid[si], t0 + kDepth * kTB));
+    pid[si] = lane_raw(t0 + 2 * kDepth * kTB);
 
-    // a4: S^T = K Q^T for the block's 16 tokens
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // a4: S^T = K Q^T for the block's 16 tokens.  All K operand reads go first, then
+    // two independent MFMA chains (even and odd k-steps): one LDS round trip and half
+    // the accumulator dependence per block, which matters at one wave per SIMD.
     const uint8_t* kp = &kt[buf][n * G::RS + hoff + 16 * j];
+    u32x4 kk[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 64 * ks)), qB[ks], sacc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) kk[ks] = *reinterpret_cast<const u32x4*>(kp + 64 * ks);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sacc0 = {0.f, 0.f, 0.f, 0.f}, sacc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[ks]), qB[ks], sacc0, 0, 0, 0);
+      sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[ks + 1]), qB[ks + 1], sacc1, 0, 0, 0);
+    }
+    const f32x4 sacc = sacc0 + sacc1;
 
     // online softmax: lane holds row n's scores for tokens 4j + r
     float sc[4];
@@ -208,14 +250,23 @@ __global__ __launch_bounds__(64 * HPC * NRG) void splitkv_tile_kernel(FwdParams 
     // a5: O^T += V^T P^T, V^T from transposed LDS reads
     __attribute__((address_space(3))) char* vb =
         (__attribute__((address_space(3))) char*)vt[buf] + vlane;
+    // all transposed reads first, then the MFMAs (one LDS round trip per block)
+    i16x4 va[CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(vb + 32 * ct));
-      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB, oacc[ct], 0, 0, 0);
-    }
+    for (int ct = 0; ct < CT; ++ct)
+      va[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(vb + 32 * ct));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], pB, oacc[ct], 0, 0, 0);
 
-    if (blk + 1 < nblk) stage(buf ^ 1);
+    stage(std::integral_constant<int, (decltype(set)::value + 1) % kDepth>{}, buf ^ 1);
     __syncthreads();
+  };
+  for (int blk = 0; blk < nblk; blk += kDepth) {
+    step(S0{}, blk);
+    step(S1{}, blk + 1);
+    step(S2{}, blk + 2);
   }
 
   // each lane summed only its own tokens: total the 4 lanes of the row

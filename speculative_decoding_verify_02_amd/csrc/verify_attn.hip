@@ -140,10 +140,9 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
     p->hpc = 1;
     while (p->hpc * 2 <= max_hpc && a->hkv % (p->hpc * 2) == 0) p->hpc *= 2;
     head_groups = a->hkv / p->hpc;
-    // two workgroups share a CU when both LDS tile pairs fit (16 tokens x (hpc x 512 B
-    // + 16) x 4 buffers <= 80 KB) and the 16-row waves stay within 256 registers
-    const int tile_lds = 16 * (p->hpc * 2 * a->qk_dim + 16) * 4;
-    per_cu = (tile_lds <= 80 * 1024 && p->nrg >= 2) ? 2 : 1;
+    // one workgroup per CU: three blocks in flight in registers take a wave's whole
+    // register file
+    per_cu = 1;
   } else {
     p->kind = kGeneric;
     p->rt = (rows <= 16) ? 1 : (a->v_dim <= 256 ? 2 : 1);
