@@ -163,21 +163,32 @@ struct PieceWalk {
   int64_t a, e, q, cum;
   int b, y, len;
 
-  // Finds row y's first piece.  Returns false when the row has no keys.
+  __device__ int keys_of(const FwdParams& P, int c) const {
+    return seq_len_keys(P, c, seq_prefix_len(P, c));
+  }
+
+  // Finds row y's first piece.  Returns false when the row has no keys.  The key
+  // counts of the first 64 sequences are loaded once (lane s: sequence s) and serve
+  // both passes.
   __device__ bool init(const FwdParams& P, int row) {
     const int lane = threadIdx.x & 63;
     y = row;
     if (P.slots == 1) {
-      if (y >= P.batch || seq_len_keys(P, y, seq_prefix_len(P, y)) == 0) return false;
+      if (y >= P.batch || keys_of(P, y) == 0) return false;
       b = y;
       q = 0;
       return true;
     }
+    const int ln0 = lane < P.batch ? keys_of(P, lane) : 0;
     int64_t T = 0;
     int mx = 0;
     for (int c = 0; c < P.batch; c += 64) {
       int l = 0;
-      if (c + lane < P.batch) l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
+      if (c == 0) {
+        l = ln0;
+      } else if (c + lane < P.batch) {
+        l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
+      }
       int64_t sum = l;
       int m = l;
 #pragma unroll
@@ -203,7 +214,11 @@ struct PieceWalk {
     int64_t base = 0;
     for (int c = 0; c < P.batch; c += 64) {
       int l = 0;
-      if (c + lane < P.batch) l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
+      if (c == 0) {
+        l = ln0;
+      } else if (c + lane < P.batch) {
+        l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
+      }
       int64_t incl = l;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -256,7 +271,7 @@ struct PieceWalk {
     // the next sequence with keys (sequences without rows own none)
     while (cum < e && b + 1 < P.batch) {
       ++b;
-      len = seq_len_keys(P, b, seq_prefix_len(P, b));
+      len = keys_of(P, b);
       if (len > 0) return true;
     }
     return false;
