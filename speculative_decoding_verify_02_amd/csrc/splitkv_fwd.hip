@@ -579,6 +579,7 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.window = a->window_left;
   fp.slots = p.slots;
   fp.min_q = p.min_q;
+  fp.piece_cost = p.piece_cost;
   fp.c_log2 = a->sm_scale * a->k_scale * kLog2e;
   fp.v_scale = a->v_scale;
   fp.qo_indptr = a->qo_indptr;

@@ -35,6 +35,7 @@ struct Plan {
   int slots;        // partial slots per (sequence, KV head): the split count S
   int nwy;          // workgroups along grid y (token ranges)
   int min_q;        // fewest tokens one workgroup is given
+  int piece_cost;   // fixed cost of one piece, in keys of the kernel's main loop
   int max_leff;     // host bound of the attended prefix length
   int64_t ws_o_floats;    // offset of partial LSEs in the workspace (floats)
   int64_t ws_cnt_floats;  // offset of the per-sequence piece counts (int32)
@@ -56,6 +57,7 @@ struct FwdParams {
   int32_t* counts;   // [B] pieces written per sequence
   int batch, hkv, group, draft, rows, lg_page, window;
   int slots, min_q;
+  int piece_cost;  // fixed cost of one piece in keys (cost-balanced partition)
   float c_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
   // extensions (NULL / 0: off)
@@ -112,18 +114,25 @@ __device__ __forceinline__ float cap_log2(float x, float cap) {
 // Sequence b owns len_b = (L_b - lo_b) + n_b keys: its attended prefix [lo_b, L_b)
 // (lo_b = max(0, L_b - W) with a left window W, else 0) and then its n_b draft keys
 // (n_b = D, or qo[b+1] - qo[b] with ragged rows), which sit in the paged cache
-// right after the prefix (tree verify: D draft keys at draft_slots).  The sequences' keys are
-// laid end to end (T in all) and cut into ranges of
+// right after the prefix (tree verify: D draft keys at draft_slots).
+//
+// Cost-balanced ranges: a piece has a fixed cost (q load, the first tile's latency,
+// the partial write) worth C = piece_cost keys of the main loop, so each sequence
+// is given C virtual keys in front of its real ones (vlen_b = C + len_b, 0 for a
+// sequence without keys).  The virtual keys of all sequences are laid end to end
+// (T in all) and cut into ranges of
 //     q = max(ceil(T / nwy), ceil(max_b len_b / (slots - 1)), min_q)
-// keys, range y going to the workgroups of grid row y (one per head group), so
-// every workgroup streams about the same number of keys whatever the length mix.
-// A range is cut at sequence ends into pieces.  Sequence b's pieces come from
-// consecutive rows first_b .. last_b with first_b = floor(cum_b / q) and last_b =
-// floor((cum_b + len_b - 1) / q); the piece of row y writes partial slot
-// y - first_b, and the row holding the last piece records the count.  A sequence
-// spans at most floor((len_b - 1) / q) + 2 <= slots rows, whatever the device
-// lengths are, so the slots never overflow.  With slots == 1 row y takes all of
-// sequence y.  Only host scalars size the grid; lengths are read on the device.
+// keys, range y going to the workgroups of grid row y (one per head group).  A
+// range is cut at sequence ends into pieces (its virtual keys are no work), so a
+// workgroup whose range starts a second sequence gets C fewer real keys, and every
+// workgroup carries about the same cost whatever the length mix.  Sequence b's real
+// keys occupy [s_b, s_b + len_b) with s_b = cum_b + C; its pieces come from
+// consecutive rows first_b = floor(s_b / q) .. last_b = floor((s_b + len_b - 1) / q),
+// the piece of row y writes partial slot y - first_b, and the row holding the last
+// piece records the count.  A sequence spans at most floor((len_b - 1) / q) + 2 <=
+// slots rows, whatever the device lengths are, so the slots never overflow.  With
+// slots == 1 row y takes all of sequence y.  Only host scalars size the grid;
+// lengths are read on the device.
 struct Piece {
   int b;       // sequence
   int L;       // its prefix length
@@ -160,16 +169,17 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 }
 
 struct PieceWalk {
-  int64_t a, e, q, cum;
+  int64_t a, e, q, cum;  // range [a, e) and sequence b's virtual start, in virtual keys
   int b, y, len;
 
   __device__ int keys_of(const FwdParams& P, int c) const {
     return seq_len_keys(P, c, seq_prefix_len(P, c));
   }
+  __device__ int64_t vlen(const FwdParams& P, int l) const { return l > 0 ? (int64_t)l + P.piece_cost : 0; }
 
-  // Finds row y's first piece.  Returns false when the row has no keys.  The key
-  // counts of the first 64 sequences are loaded once (lane s: sequence s) and serve
-  // both passes.
+  // Finds row y's first piece.  Returns false when the row has no real keys.  The
+  // key counts of the first 64 sequences are loaded once (lane s: sequence s) and
+  // serve both passes.
   __device__ bool init(const FwdParams& P, int row) {
     const int lane = threadIdx.x & 63;
     y = row;
@@ -189,7 +199,7 @@ struct PieceWalk {
       } else if (c + lane < P.batch) {
         l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
       }
-      int64_t sum = l;
+      int64_t sum = vlen(P, l);
       int m = l;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) {
@@ -210,7 +220,7 @@ struct PieceWalk {
     a = (int64_t)y * q;
     if (a >= T) return false;
     e = a + q < T ? a + q : T;
-    // the sequence holding key a: inclusive scan of len over 64 sequences at a time
+    // the sequence holding virtual key a: inclusive scan over 64 sequences at a time
     int64_t base = 0;
     for (int c = 0; c < P.batch; c += 64) {
       int l = 0;
@@ -219,7 +229,8 @@ struct PieceWalk {
       } else if (c + lane < P.batch) {
         l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
       }
-      int64_t incl = l;
+      const int64_t vl = vlen(P, l);
+      int64_t incl = vl;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int64_t t = __shfl_up(incl, off, 64);
@@ -229,8 +240,9 @@ struct PieceWalk {
       if (hit) {
         const int f = __builtin_ctzll(hit);
         b = c + f;
-        cum = uniform64(base + __shfl(incl, f, 64) - __shfl(l, f, 64));
-        return true;
+        cum = uniform64(base + __shfl(incl, f, 64) - __shfl(vl, f, 64));
+        // a range that ends inside b's virtual keys holds no real key
+        return cum + P.piece_cost < e;
       }
       base += __shfl(incl, 63, 64);
     }
@@ -250,11 +262,12 @@ struct PieceWalk {
       pc.count = 1;
       return pc;
     }
-    const int64_t s0 = a > cum ? a : cum;
-    const int64_t s1 = e < cum + len ? e : cum + len;
-    pc.t0 = lo + (int)(s0 - cum);
-    pc.t1 = lo + (int)(s1 - cum);
-    const int64_t first = cum / q, last = (cum + len - 1) / q;
+    const int64_t sb = cum + P.piece_cost;  // virtual position of b's first real key
+    const int64_t s0 = a > sb ? a : sb;
+    const int64_t s1 = e < sb + len ? e : sb + len;
+    pc.t0 = lo + (int)(s0 - sb);
+    pc.t1 = lo + (int)(s1 - sb);
+    const int64_t first = sb / q, last = (sb + len - 1) / q;
     pc.slot = (int)(y - first);
     pc.count = (y == last) ? (int)(last - first + 1) : 0;
     pc.t0 = __builtin_amdgcn_readfirstlane(pc.t0);
@@ -264,15 +277,15 @@ struct PieceWalk {
     return pc;
   }
 
-  // Advances to the next sequence of the range; false at its end.
+  // Advances to the next sequence of the range with real keys in it; false at its end.
   __device__ bool next(const FwdParams& P) {
     if (P.slots == 1) return false;
-    cum += len;
+    cum += vlen(P, len);
     // the next sequence with keys (sequences without rows own none)
     while (cum < e && b + 1 < P.batch) {
       ++b;
       len = keys_of(P, b);
-      if (len > 0) return true;
+      if (len > 0) return cum + P.piece_cost < e;
     }
     return false;
   }

@@ -163,6 +163,9 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
   p->max_leff = max_attended_prefix(a->max_prefix_len, a->window_left);
   // fewest keys per workgroup: a few blocks of the kernel's main loop
   p->min_q = p->kind == kMlaFp8 ? 128 : (p->kind == kTile ? 64 : 64);
+  // fixed cost of a piece in keys of the main loop (q load, the first block's memory
+  // latency, the partial write), from per-wave timings of one- and two-piece ranges
+  p->piece_cost = p->kind == kMlaFp8 ? 704 : (p->kind == kTile ? 80 : 32);
   const long long maxlen = (long long)p->max_leff + a->draft_len;
   const int maxlen_i = maxlen > INT32_MAX ? INT32_MAX : (int)maxlen;
   int nwy = 1, slots = 1;
