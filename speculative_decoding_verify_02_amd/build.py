@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     "-shared",
     # hipcc's own packed-fp32 code generation is switched off for every HIP source
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: with AGPR accumulators the online
+    # softmax rescale copies every O register out and back each key block
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "va_internal.h"
 
@@ -34,6 +35,7 @@ namespace va {
 namespace {
 
 constexpr int kTB = 16;  // tokens per block
+constexpr float kLazy = 8.f;  // log2 headroom of the running max (p <= 256)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
@@ -46,8 +48,13 @@ template <int D, int HPC, int NRG>
 struct TileGeo {
   static constexpr int W = HPC * NRG;             // waves per workgroup
   static constexpr int RB = D * 2;                // bytes of one head's row
-  static constexpr int RS = HPC * RB + 16;        // LDS row stride (pad: conflict-free reads)
-  static constexpr int TILE = kTB * RS;           // bytes of one K (or V) tile
+  // LDS row strides, padded so that reads hit every bank once per pass: a K read has
+  // 16 lanes on 16 rows (rows 4 banks apart), a transposed V read 32 lanes on 8 rows
+  // of 8 banks each (rows 8 banks apart)
+  static constexpr int RSK = HPC * RB + 16;
+  static constexpr int RSV = HPC * RB + 32;
+  static constexpr int TILEK = kTB * RSK;         // bytes of one K tile
+  static constexpr int TILEV = kTB * RSV;         // bytes of one V tile
   static constexpr int CH = HPC * RB / 16;        // 16-byte chunks per token row slice
   static constexpr int NLD = kTB * CH / (64 * W); // loads per thread per block (K; same for V)
   static_assert((kTB * CH) % (64 * W) == 0, "whole loads per thread");
@@ -57,18 +64,25 @@ struct TileGeo {
 
 constexpr int kDepth = 3;  // blocks in flight in registers
 
+// f(integral_constant<int, I>) for each I of the sequence, in order: every register
+// set of the block ring gets a fixed name in the unrolled loop.
+template <class F, int... I>
+__device__ __forceinline__ void for_sets(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
 template <int D, int HPC, int NRG>
 __global__ __launch_bounds__(64 * HPC * NRG) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void splitkv_tile_kernel(FwdParams P) {
   using G = TileGeo<D, HPC, NRG>;
   constexpr int KS = D / 32;   // QK k-steps
   constexpr int CT = D / 16;   // O^T column tiles
-  __shared__ __attribute__((aligned(16))) uint8_t kt[2][G::TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[2][G::TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][G::TILEK];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[2][G::TILEV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int j = lane >> 4;
   const int hc = wave / NRG;          // head within the workgroup
@@ -78,6 +92,17 @@ void splitkv_tile_kernel(FwdParams P) {
   PieceWalk pw;
   if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
   const int row = rg * 16 + n;
+  // this thread's load chunks: q = 64*W*u + tid -> token q / CH, head (q % CH) / (RB/16),
+  // 16-byte chunk (q % CH) % (RB/16) of that head's row
+  const uint32_t k_sslot = (uint32_t)P.k_sslot, v_sslot = (uint32_t)P.v_sslot;
+  uint32_t koff[G::NLD], voff[G::NLD];
+#pragma unroll
+  for (int u = 0; u < G::NLD; ++u) {
+    const int c = (64 * G::W * u + tid) % G::CH;
+    const int hd = c / (G::RB / 16), cc = c % (G::RB / 16);
+    koff[u] = (uint32_t)((g0 + hd) * (uint32_t)P.k_shead + 16 * cc);
+    voff[u] = (uint32_t)((g0 + hd) * (uint32_t)P.v_shead + 16 * cc);
+  }
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
 
@@ -112,6 +137,18 @@ void splitkv_tile_kernel(FwdParams P) {
   // keys of row i: p - W <= t <= p with p = L + i (prefix and causal draft keys)
   const int row_lo = (P.window >= 0 && rv) ? L + row_i - P.window : INT_MIN;
   const int row_hi = rv ? (tree ? t_last : min(t_last, L + row_i)) : -1;
+  // keys every row of the wave sees: blocks inside [wave_lo, wave_hi] need no masking
+  // (tree draft keys and capped logits always take the general path)
+  int wave_lo = rv ? row_lo : INT_MIN;
+  int wave_hi = rv ? (tree ? min(row_hi, L - 1) : row_hi) : INT_MAX;
+  if (P.logit_cap > 0.f) wave_hi = INT_MIN;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    wave_lo = max(wave_lo, __shfl_xor(wave_lo, off, 64));
+    wave_hi = min(wave_hi, __shfl_xor(wave_hi, off, 64));
+  }
+  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[CT];
@@ -119,7 +156,6 @@ void splitkv_tile_kernel(FwdParams P) {
   for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-  // this thread's load chunks: q = 64*W*u + tid -> token q / CH, head (q % CH) / (RB/16)
   // A slot lookup in two parts: lane_raw loads the page id of the lane's token of the
   // block at t0 (its draft slot for tree-verify draft keys) with no branch, and
   // lane_slot turns it into the slot where the value is used, so the wait for the
@@ -127,7 +163,9 @@ void splitkv_tile_kernel(FwdParams P) {
   auto lane_raw = [&](int t0) -> int {
     const int t = min(t0 + (lane & (kTB - 1)), t_last);
     const int32_t* src = (tree && t >= L) ? P.draft_slots + b * P.draft + (t - L) : bt_row + (t >> lg);
-    return *src;
+    // a global (not flat) load: the compiler then waits for it by count and leaves
+    // the data loads issued after it in flight
+    return *(const __attribute__((address_space(1))) int32_t*)src;
   };
   auto lane_slot = [&](int raw, int t0) -> int {
     const int t = min(t0 + (lane & (kTB - 1)), t_last);
@@ -135,53 +173,67 @@ void splitkv_tile_kernel(FwdParams P) {
   };
   // kDepth register sets: set s holds the blocks b with b % kDepth == s
   u32x4 kr[kDepth][G::NLD], vr[kDepth][G::NLD];
-  auto load = [&](auto set, int sl_lane) {
+  // Slot s's row starts s * sslot bytes into the cache (the host checks that slot
+  // strides and head offsets fit in 32 bits).  When a token row is a whole number of
+  // wave loads (CH a multiple of 64), every load instruction of a wave reads one
+  // token, so its slot and base address are scalar and the lane adds only its
+  // 32-bit offset inside the row.
+  auto load_part = [&](auto set, int sl_lane, int u0, int u1) {
 #pragma unroll
-    for (int u = 0; u < G::NLD; ++u) {
-      const int q = 64 * G::W * u + tid;
-      const int tok = q / G::CH, c = q % G::CH;
-      const int hd = c / (G::RB / 16), cc = c % (G::RB / 16);
-      const int64_t slot = __shfl(sl_lane, tok, 64);
-      kr[set][u] = *reinterpret_cast<const u32x4*>(P.k + slot * P.k_sslot + (int64_t)(g0 + hd) * P.k_shead + 16 * cc);
-      vr[set][u] = *reinterpret_cast<const u32x4*>(P.v + slot * P.v_sslot + (int64_t)(g0 + hd) * P.v_shead + 16 * cc);
+    for (int u = u0; u < u1; ++u) {
+      uint32_t slot;
+      if constexpr (G::CH % 64 == 0) {
+        slot = __builtin_amdgcn_readlane(sl_lane, (G::W * u + wave) / (G::CH / 64));
+      } else {
+        slot = __shfl(sl_lane, (64 * G::W * u + tid) / G::CH, 64);
+      }
+      kr[set][u] = *reinterpret_cast<const u32x4*>(P.k + (uint64_t)slot * k_sslot + koff[u]);
+      vr[set][u] = *reinterpret_cast<const u32x4*>(P.v + (uint64_t)slot * v_sslot + voff[u]);
     }
+  };
+  auto load = [&](auto set, int sl_lane) { load_part(set, sl_lane, 0, G::NLD); };
+  // a step issues its block's loads in kParts groups spread over the step, so the
+  // CU's vector memory path works while the waves compute
+  constexpr int kParts = G::NLD < 4 ? G::NLD : 4;
+  auto load_q = [&](auto set, int sl_lane, int part) {
+    load_part(set, sl_lane, part * G::NLD / kParts, (part + 1) * G::NLD / kParts);
   };
   auto stage = [&](auto set, int buf) {
 #pragma unroll
     for (int u = 0; u < G::NLD; ++u) {
       const int q = 64 * G::W * u + tid;
-      const int off = (q / G::CH) * G::RS + 16 * (q % G::CH);
-      *reinterpret_cast<u32x4*>(&kt[buf][off]) = kr[set][u];
-      *reinterpret_cast<u32x4*>(&vt[buf][off]) = vr[set][u];
+      const int tok = q / G::CH, c16 = 16 * (q % G::CH);
+      *reinterpret_cast<u32x4*>(&kt[buf][tok * G::RSK + c16]) = kr[set][u];
+      *reinterpret_cast<u32x4*>(&vt[buf][tok * G::RSV + c16]) = vr[set][u];
     }
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  static_assert(kDepth == 3, "the loop below is unrolled by three");
+  using Sets = std::make_integer_sequence<int, kDepth>;
 
   // Page ids: at step b (set s = b % kDepth), pid[s] holds block b + kDepth's and is
   // refilled with block b + 2 kDepth's once used.  A lookup is issued kDepth steps
   // before its use and each register is written and read once per kDepth steps, so
   // the compiler's wait for a lookup leaves the later steps' data loads in flight.
-  int pid[kDepth] = {0, 0, 0};
+  int pid[kDepth];
   {
-    const int s0 = lane_raw(t_begin);
-    const int s1 = lane_raw(t_begin + kTB);
-    const int s2 = lane_raw(t_begin + 2 * kTB);
+    int first[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) first[u] = lane_raw(t_begin + u * kTB);
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) pid[u] = lane_raw(t_begin + (kDepth + u) * kTB);
-    load(S0{}, lane_slot(s0, t_begin));
-    load(S1{}, lane_slot(s1, t_begin + kTB));
-    load(S2{}, lane_slot(s2, t_begin + 2 * kTB));
-    stage(S0{}, 0);
+    for_sets(
+        [&](auto set) {
+          constexpr int u = decltype(set)::value;
+          load(set, lane_slot(first[u], t_begin + u * kTB));
+        },
+        Sets{});
+    stage(std::integral_constant<int, 0>{}, 0);
   }
   __syncthreads();
 
   const int hoff = hc * G::RB;
   // transposed-read address of this lane inside a V tile: token row 4j + n/4, 4
   // columns starting at 4*(n%4) of each 16-column tile
-  const int vlane = (4 * j + (n >> 2)) * G::RS + hoff + 8 * (n & 3);
+  const int vlane = (4 * j + (n >> 2)) * G::RSV + hoff + 8 * (n & 3);
 
   // One block: its set refills with block blk + kDepth, the block is computed from
   // LDS, and block blk + 1 is staged into the other LDS tile.  Steps have no
@@ -192,13 +244,13 @@ void splitkv_tile_kernel(FwdParams P) {
     const int buf = blk & 1;
     const int t0 = t_begin + blk * kTB;
     constexpr int si = decltype(set)::value;
-    load(set, lane_slot(pid[si], t0 + kDepth * kTB));
-    pid[si] = lane_raw(t0 + 2 * kDepth * kTB);
+    const int sl_next = lane_slot(pid[si], t0 + kDepth * kTB);
+    load_q(set, sl_next, 0);
 
     // a4: S^T = K Q^T for the block's 16 tokens.  All K operand reads go first, then
     // two independent MFMA chains (even and odd k-steps): one LDS round trip and half
     // the accumulator dependence per block, which matters at one wave per SIMD.
-    const uint8_t* kp = &kt[buf][n * G::RS + hoff + 16 * j];
+    const uint8_t* kp = &kt[buf][n * G::RSK + hoff + 16 * j];
     u32x4 kk[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kk[ks] = *reinterpret_cast<const u32x4*>(kp + 64 * ks);
@@ -209,28 +261,33 @@ void splitkv_tile_kernel(FwdParams P) {
       sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[ks]), qB[ks], sacc0, 0, 0, 0);
       sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk[ks + 1]), qB[ks + 1], sacc1, 0, 0, 0);
     }
+    if constexpr (kParts > 1) load_q(set, sl_next, 1);
     const f32x4 sacc = sacc0 + sacc1;
 
     // online softmax: lane holds row n's scores for tokens 4j + r
     float sc[4];
-    float bmax = -INFINITY;
+    if (t0 >= wave_lo && t0 + (kTB - 1) <= wave_hi) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 4 * j + r;
-      const bool ok = key_ok(t, row_lo, row_hi, L, tbits, tree);
-      sc[r] = ok ? sacc[r] * P.c_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * P.c_log2;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * j + r;
+        const bool ok = key_ok(t, row_lo, row_hi, L, tbits, tree);
+        sc[r] = ok ? sacc[r] * P.c_log2 : -INFINITY;
+      }
+      if (P.logit_cap > 0.f) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = sc[r] == -INFINITY ? sc[r] : cap_log2(sc[r], P.logit_cap);
+      }
     }
-    if (P.logit_cap > 0.f) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = sc[r] == -INFINITY ? sc[r] : cap_log2(sc[r], P.logit_cap);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, sc[r]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m_run, bmax);
+    const float bmax = rows4_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    // the reference max moves only when a score passes it by more than kLazy, so
+    // most blocks leave the accumulator alone; p = 2^(s - m) stays <= 2^kLazy
+    const bool grow = bmax > m_run + kLazy;
+    const float m_new = grow ? bmax : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -239,7 +296,7 @@ void splitkv_tile_kernel(FwdParams P) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    if (__any(alpha != 1.f)) {
+    if (__any(grow)) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) oacc[ct] *= alpha;
     }
@@ -247,6 +304,7 @@ void splitkv_tile_kernel(FwdParams P) {
     const s16x4 pB = {__builtin_bit_cast(short, p0), __builtin_bit_cast(short, p1),
                       __builtin_bit_cast(short, p2), __builtin_bit_cast(short, p3)};
 
+    if constexpr (kParts > 2) load_q(set, sl_next, 2);
     // a5: O^T += V^T P^T, V^T from transposed LDS reads
     __attribute__((address_space(3))) char* vb =
         (__attribute__((address_space(3))) char*)vt[buf] + vlane;
@@ -260,18 +318,16 @@ void splitkv_tile_kernel(FwdParams P) {
     for (int ct = 0; ct < CT; ++ct)
       oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[ct], pB, oacc[ct], 0, 0, 0);
 
+    if constexpr (kParts > 3) load_q(set, sl_next, 3);
+    pid[si] = lane_raw(t0 + 2 * kDepth * kTB);
     stage(std::integral_constant<int, (decltype(set)::value + 1) % kDepth>{}, buf ^ 1);
     __syncthreads();
   };
-  for (int blk = 0; blk < nblk; blk += kDepth) {
-    step(S0{}, blk);
-    step(S1{}, blk + 1);
-    step(S2{}, blk + 2);
-  }
+  for (int blk = 0; blk < nblk; blk += kDepth)
+    for_sets([&](auto set) { step(set, blk + decltype(set)::value); }, Sets{});
 
   // each lane summed only its own tokens: total the 4 lanes of the row
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = rows4_sum(l_run);
   if (rv) {
     const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
     const float inv = l_run > 0.f ? P.v_scale / l_run : 0.f;
@@ -306,9 +362,13 @@ int launch_d(const FwdParams& fp, int hpc, int nrg, dim3 grid, hipStream_t st) {
       return VA_EUNSUPPORTED;
     case 12: VA_TILE(1, 2);
     case 22: VA_TILE(2, 2);
-    case 42: VA_TILE(4, 2);
+    case 42:
+      if constexpr (D == 128) { VA_TILE(4, 2); }  // d = 256 takes at most 4 waves
+      return VA_EUNSUPPORTED;
     case 14: VA_TILE(1, 4);
-    case 24: VA_TILE(2, 4);
+    case 24:
+      if constexpr (D == 128) { VA_TILE(2, 4); }
+      return VA_EUNSUPPORTED;
     default: return VA_EUNSUPPORTED;
   }
 #undef VA_TILE

@@ -108,6 +108,24 @@ __device__ __forceinline__ float cap_log2(float x, float cap) {
   return (cap * kLog2e) * (e - 1.f) * __builtin_amdgcn_rcpf(e + 1.f);
 }
 
+// Max and sum over the four lanes n, n + 16, n + 32, n + 48 of a wave (one score row
+// spread over the four 16-lane rows of an MFMA output), with gfx950's row swaps:
+// permlane16_swap of x with itself leaves x of rows {0, 1} (and {2, 3}) in the two
+// results of each lane of the pair, permlane32_swap those of rows {0, 2} and {1, 3}.
+// Every lane of the group gets the bit-identical result.  No LDS round trip.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Work partition of the split-KV pass (device side, identical in every wave).
 //

@@ -24,6 +24,16 @@ int ilog2(int x) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Byte offsets of a slot row and of the last KV head inside it fit in 32 bits (the
+// tile kernel adds slot * slot stride as one 32 x 32 -> 64-bit product and keeps the
+// in-row offset in 32 bits).
+bool slot_offsets_fit_32(const verify_attn_args* a) {
+  const int64_t lim = (int64_t)1 << 31;
+  return a->k_stride_slot * 2 < lim && a->v_stride_slot * 2 < lim &&
+         ((int64_t)a->hkv * a->k_stride_head + a->qk_dim) * 2 < lim &&
+         ((int64_t)a->hkv * a->v_stride_head + a->v_dim) * 2 < lim;
+}
+
 bool supported_dims(int qk, int v) {
   return (qk == 128 && v == 128) || (qk == 256 && v == 256) || (qk == 576 && v == 512);
 }
@@ -129,7 +139,8 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
     p->nrg = 4;
     p->ntl = 1;
     p->hpc = 1;
-  } else if (!fp8 && a->qk_dim == 256 && a->v_dim == 256 && rows <= 64) {
+  } else if (!fp8 && a->qk_dim == 256 && a->v_dim == 256 && rows <= 64 &&
+             slot_offsets_fit_32(a)) {
     // wide bf16 heads: whole-slot-row tiles (d = 128 streams better per wave)
     p->kind = kTile;
     p->rt = 1;
