@@ -100,18 +100,18 @@ __device__ __forceinline__ int slot_token(int j, int i) { return 16 * (i >> 2) +
 
 template <class G>
 __device__ __forceinline__ void load_block(KVRegs<G>& R, int lslot, const uint8_t* kg,
-                                           const uint8_t* vg, int64_t k_sslot, int64_t v_sslot,
+                                           const uint8_t* vg, uint32_t k_sslot, uint32_t v_sslot,
                                            int lane, int n, int j) {
 #pragma unroll
   for (int u = 0; u < G::NKLD; ++u) {
     const int q = 64 * u + lane;
     const int sl = __shfl(lslot, q / G::KCH, 64);
-    R.k[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)sl * k_sslot + 16 * (q % G::KCH));
+    R.k[u] = *reinterpret_cast<const u32x4*>(kg + (uint64_t)(uint32_t)sl * k_sslot + 16 * (q % G::KCH));
   }
 #pragma unroll
   for (int i = 0; i < 4 * G::TB / 16; ++i) {
     const int sl = __shfl(lslot, slot_token(j, i), 64);
-    const uint8_t* vp = vg + (int64_t)sl * v_sslot + G::VGB * n;
+    const uint8_t* vp = vg + (uint64_t)(uint32_t)sl * v_sslot + G::VGB * n;
 #pragma unroll
     for (int c = 0; c < G::VG; ++c) {
       if constexpr (G::VGB == 16) {
@@ -312,6 +312,8 @@ void splitkv_fwd_kernel(FwdParams P) {
   if (!pw.init(P, blockIdx.y)) return;  // uniform over the workgroup, before any barrier
   const uint8_t* kg = P.k + (int64_t)g * P.k_shead;
   const uint8_t* vg = P.v + (int64_t)g * P.v_shead;
+  // slot s's row is s * sslot bytes in (the host checks that a slot stride fits in 32 bits)
+  const uint32_t k_sslot = (uint32_t)P.k_sslot, v_sslot = (uint32_t)P.v_sslot;
   uint8_t* tile = s_tile[wave];
   const int lg = P.lg_page;
   const int pmask = (1 << lg) - 1;
@@ -379,33 +381,46 @@ void splitkv_fwd_kernel(FwdParams P) {
   int blk = tl;
   if (blk < nblk) {
     if constexpr (PIPE) {
-      // next block's K/V loads in flight while a block computes (register sets A/B)
-      int sl_next = 0, sl_after = 0;
-      const int sl0 = lslot(t0_of(blk));
-      if (blk + NTL < nblk) sl_next = lslot(t0_of(blk + NTL));
+      // Block blk + NTL's K/V loads are in flight while block blk computes (register
+      // sets A/B).  A page-id lookup is issued before the data loads of the block
+      // before it and used a half step later, so the compiler's wait for it never
+      // counts data loads still in flight.  The steps have no branches: a block past
+      // the piece loads its last token (a valid address) and is never computed
+      // masked, so the compiler keeps exact counts of the loads in flight.  The loop
+      // takes blocks in pairs; a last odd block is computed after it.
+      auto lraw = [&](int t0) -> int {
+        const int t = min(t0 + (lane & (TB - 1)), t_last);
+        const int32_t* src = (EXT && mk.tree && t >= L) ? P.draft_slots + b * P.draft + (t - L)
+                                                        : bt_row + (t >> lg);
+        return *(const __attribute__((address_space(1))) int32_t*)src;
+      };
+      auto rslot = [&](int raw, int t0) -> int {
+        const int t = min(t0 + (lane & (TB - 1)), t_last);
+        return (EXT && mk.tree && t >= L) ? raw : (raw << lg) | (t & pmask);
+      };
       KVRegs<G> A, Bk;
-      load_block<G>(A, sl0, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
+      const int raw0 = lraw(t0_of(blk));
+      int raw1 = lraw(t0_of(blk + NTL));
+      load_block<G>(A, rslot(raw0, t0_of(blk)), kg, vg, k_sslot, v_sslot, lane, n, j);
+      int raw2 = lraw(t0_of(blk + 2 * NTL));
       stage_k<G>(A, tile, lane);
-      for (;;) {
-        const int b1 = blk + NTL, b2 = blk + 2 * NTL;
-        if (b1 < nblk) load_block<G>(Bk, sl_next, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
-        if (b2 < nblk) sl_after = lslot(t0_of(b2));
+      for (; blk + NTL < nblk; blk += 2 * NTL) {
+        load_block<G>(Bk, rslot(raw1, t0_of(blk + NTL)), kg, vg, k_sslot, v_sslot, lane, n, j);
+        raw1 = lraw(t0_of(blk + 3 * NTL));
         compute_block<G, FP8, RT, DV, EXT>(tile, A, qB, mk, st, t0_of(blk), n, j);
-        if (b1 >= nblk) break;
         stage_k<G>(Bk, tile, lane);
-        const int b3 = blk + 3 * NTL;
-        if (b2 < nblk) load_block<G>(A, sl_after, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
-        if (b3 < nblk) sl_next = lslot(t0_of(b3));
-        compute_block<G, FP8, RT, DV, EXT>(tile, Bk, qB, mk, st, t0_of(b1), n, j);
-        if (b2 >= nblk) break;
+        load_block<G>(A, rslot(raw2, t0_of(blk + 2 * NTL)), kg, vg, k_sslot, v_sslot, lane, n, j);
+        raw2 = lraw(t0_of(blk + 4 * NTL));
+        compute_block<G, FP8, RT, DV, EXT>(tile, Bk, qB, mk, st, t0_of(blk + NTL), n, j);
         stage_k<G>(A, tile, lane);
-        blk = b2;
       }
+      // an odd block count leaves one block, already staged in A
+      if (blk < nblk) compute_block<G, FP8, RT, DV, EXT>(tile, A, qB, mk, st, t0_of(blk), n, j);
     } else {
       int sl = lslot(t0_of(blk));
       for (; blk < nblk; blk += NTL) {
         KVRegs<G> A;
-        load_block<G>(A, sl, kg, vg, P.k_sslot, P.v_sslot, lane, n, j);
+        load_block<G>(A, sl, kg, vg, k_sslot, v_sslot, lane, n, j);
         if (blk + NTL < nblk) sl = lslot(t0_of(blk + NTL));
         stage_k<G>(A, tile, lane);
         compute_block<G, FP8, RT, DV, EXT>(tile, A, qB, mk, st, t0_of(blk), n, j);

@@ -127,6 +127,9 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
       return VA_EINVAL;
     if (a->o_stride_row <= 0 || a->o_stride_head <= 0) return VA_EINVAL;
     if (a->k_stride_head < a->qk_dim || a->v_stride_head < a->v_dim) return VA_EINVAL;
+    // kernels form a slot row's address as slot * (slot stride in bytes), 32 x 32 bits
+    if (a->k_stride_slot * eb >= ((int64_t)1 << 32) || a->v_stride_slot * eb >= ((int64_t)1 << 32))
+      return VA_EUNSUPPORTED;
   }
 
   p->group = group;
