@@ -81,7 +81,8 @@ __device__ __forceinline__ Cols<CPT> load_cols(const float* p) {
 template <int DV>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   constexpr int CPT = DV / 64;  // output columns per lane
-  constexpr int NB = 8;         // partial rows loaded per batch
+  constexpr bool kReuse = DV >= 512;
+  constexpr int NB = kReuse ? 12 : 8;  // partial rows loaded per batch
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int g = blockIdx.y;
@@ -101,7 +102,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   const int64_t pstride = (int64_t)P.rows * DV;
 
   // lane s holds piece s's LSE (64 pieces per pass); the first NB pieces' columns
-  // are loaded alongside, so one round trip serves the common case
+  // are loaded alongside, so one round trip serves the common case.  Wide rows
+  // (v_dim 512) reuse one register buffer for every batch, which keeps the kernel
+  // under 128 registers; narrower rows load each later batch into fresh registers.
   Cols<CPT> first[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u)
@@ -124,21 +127,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
     Z += wave_sum(w);
     const int cnt = min(64, n - s0);
     for (int s = 0; s < cnt; s += NB) {
-      Cols<CPT> vals[NB];
-      if (s0 == 0 && s == 0) {
+      if constexpr (kReuse) {
+        if (s0 > 0 || s > 0) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u) vals[u] = first[u];
+          for (int u = 0; u < NB; ++u)
+            if (s + u < cnt) first[u] = load_cols<CPT>(po + (int64_t)(s0 + s + u) * pstride);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          if (s + u >= cnt) break;
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[c] += wu * first[u].v[c];
+        }
       } else {
+        Cols<CPT> vals[NB];
+        if (s0 == 0 && s == 0) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u)
-          if (s + u < cnt) vals[u] = load_cols<CPT>(po + (int64_t)(s0 + s + u) * pstride);
-      }
+          for (int u = 0; u < NB; ++u) vals[u] = first[u];
+        } else {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        if (s + u >= cnt) break;
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+          for (int u = 0; u < NB; ++u)
+            if (s + u < cnt) vals[u] = load_cols<CPT>(po + (int64_t)(s0 + s + u) * pstride);
+        }
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].v[c];
+        for (int u = 0; u < NB; ++u) {
+          if (s + u >= cnt) break;
+          const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].v[c];
+        }
       }
     }
   }
