@@ -95,7 +95,9 @@ typedef struct verify_attn_args {
     int64_t q_stride_row, q_stride_head;
     /* K cache: row of token slot s, KV head g at k_cache + s*k_stride_slot +
        g*k_stride_head, qk_dim elements; slot s = page*P + offset (the
-       [-1, P, hkv, d] paged view of PR #23146)                                         */
+       [-1, P, hkv, d] paged view of PR #23146).  A slot stride of 4 GiB or more
+       (in bytes) is VA_EUNSUPPORTED: kernels form slot * stride as one 32 x 32-bit
+       product.                                                                         */
     const void* k_cache;
     int64_t k_stride_slot, k_stride_head;
     /* V cache, same addressing, v_dim elements.  May equal k_cache with the same

@@ -5,10 +5,12 @@
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -43,17 +45,34 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into LIB_PATH (always recompiles).  Returns the path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd: list, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into LIB_PATH (always recompiles).  Returns the path.
+
+    Each source compiles to its own object in parallel (no source calls device code
+    of another, so no relocatable device code is needed); one hipcc call links them."""
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objdir = tempfile.mkdtemp(prefix="va_build_")
+    try:
+        objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc(), *compile_flags, "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB_PATH + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB_PATH
 
 

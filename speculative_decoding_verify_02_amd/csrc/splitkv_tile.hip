@@ -1,4 +1,4 @@
-// Split-KV pass for bf16 GQA heads (qk_dim = v_dim = 128 or 256) that reads the
+// Split-KV pass for bf16 GQA heads (qk_dim = v_dim = 256) that reads the
 // paged cache as whole slot rows.
 //
 // In the [slot, H_kv, d] layout (the paged view of PR #23146) the K rows of all
@@ -346,40 +346,22 @@ void splitkv_tile_kernel(FwdParams P) {
   } while (pw.next(P));
 }
 
-namespace {
-
-template <int D>
-int launch_d(const FwdParams& fp, int hpc, int nrg, dim3 grid, hipStream_t st) {
-#define VA_TILE(H_, R_)                                                                      \
-  return launch_kernel(reinterpret_cast<const void*>(&splitkv_tile_kernel<D, H_, R_>), grid, \
+// d = 256 only (d = 128 streams better through the generic kernel); at most 4 waves
+int launch_splitkv_tile(const FwdParams& fp, int d, int hpc, int nrg, dim3 grid, hipStream_t st) {
+  if (d != 256) return VA_EUNSUPPORTED;
+#define VA_TILE(H_, R_)                                                                        \
+  return launch_kernel(reinterpret_cast<const void*>(&splitkv_tile_kernel<256, H_, R_>), grid, \
                        dim3(64 * (H_) * (R_)), fp, st)
   switch (hpc * 10 + nrg) {
     case 11: VA_TILE(1, 1);
     case 21: VA_TILE(2, 1);
     case 41: VA_TILE(4, 1);
-    case 81:
-      if constexpr (D == 128) { VA_TILE(8, 1); }  // 8 heads x 256 B rows: 132 KB of LDS
-      return VA_EUNSUPPORTED;
     case 12: VA_TILE(1, 2);
     case 22: VA_TILE(2, 2);
-    case 42:
-      if constexpr (D == 128) { VA_TILE(4, 2); }  // d = 256 takes at most 4 waves
-      return VA_EUNSUPPORTED;
     case 14: VA_TILE(1, 4);
-    case 24:
-      if constexpr (D == 128) { VA_TILE(2, 4); }
-      return VA_EUNSUPPORTED;
     default: return VA_EUNSUPPORTED;
   }
 #undef VA_TILE
-}
-
-}  // namespace
-
-int launch_splitkv_tile(const FwdParams& fp, int d, int hpc, int nrg, dim3 grid, hipStream_t st) {
-  if (d == 128) return launch_d<128>(fp, hpc, nrg, grid, st);
-  if (d == 256) return launch_d<256>(fp, hpc, nrg, grid, st);
-  return VA_EUNSUPPORTED;
 }
 
 }  // namespace va

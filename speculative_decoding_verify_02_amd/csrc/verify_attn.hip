@@ -150,7 +150,7 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
     p->nrg = (rows + 15) / 16;
     if (p->nrg == 3) p->nrg = 4;
     p->ntl = 1;
-    const int max_hpc = (a->qk_dim == 256 ? 4 : 8) / p->nrg;
+    const int max_hpc = 4 / p->nrg;  // at most 4 waves of d = 256 rows
     p->hpc = 1;
     while (p->hpc * 2 <= max_hpc && a->hkv % (p->hpc * 2) == 0) p->hpc *= 2;
     head_groups = a->hkv / p->hpc;

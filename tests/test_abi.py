@@ -110,6 +110,8 @@ def test_gate_accepts_supported_shapes():
     (dict(page_size=3), B.VA_EUNSUPPORTED),
     (dict(page_size=2048), B.VA_EUNSUPPORTED),
     (dict(hq=64, hkv=1, draft_len=4), B.VA_EUNSUPPORTED),   # 256 rows per KV head
+    (dict(k_stride_slot=1 << 31), B.VA_EUNSUPPORTED),       # 4 GiB slot rows (bf16)
+    (dict(v_stride_slot=1 << 31), B.VA_EUNSUPPORTED),
 ])
 def test_gate_rejects(kw, status):
     assert can_handle(**kw) == status
