@@ -167,6 +167,20 @@ def test_gqa_ratios_and_draft_lengths(hq, hkv, draft):
     check(p, num_splits=2)
 
 
+# bf16 d = 256 takes the whole-slot-row tile kernel; these head layouts reach each of
+# its instances (heads per workgroup x 16-row groups): 1x1, 4x1, 1x2, 2x2 with a
+# ragged last row group, 1x4, and 2x1 under a window that cuts blocks.  One head per
+# workgroup reads a token row in half a wave load (per-lane slots); two or more read
+# whole wave loads per token (scalar slots).
+@pytest.mark.parametrize("hq,hkv,draft,window", [(4, 1, 4, -1), (16, 4, 4, -1), (8, 1, 4, -1),
+                                                 (16, 2, 3, -1), (16, 1, 4, -1), (8, 2, 4, 21)])
+def test_tile_head_layouts(hq, hkv, draft, window):
+    p = W.make_problem(name="tile-layouts", batch=3, prefix_lens=[45, 700, 129], draft_len=draft,
+                       hq=hq, hkv=hkv, qk_dim=256, v_dim=256, page_size=16, window_left=window,
+                       seed=650 + hq + 3 * hkv + draft + max(window, 0))
+    check(p, num_splits=3)
+
+
 @pytest.mark.parametrize("dims", [0, 1, 2])
 def test_poisoned_pool_is_never_read(dims):
     hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
