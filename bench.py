@@ -36,6 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# dense matrix-core peaks of MI355X (TFLOP/s): the bf16 MFMA serves bf16 KV, the fp8
+# MFMA the fp8 MLA kernel
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 CACHE_BYTES = 256 << 20
 
 
@@ -184,7 +187,10 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides
         step_gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
         fwd_gbs=fwd_bytes / (fwd_ms * 1e-3) / 1e9,
         kernels_gbs=kv_bytes / ((bt_ms + fwd_ms + comb_ms) * 1e-3) / 1e9,
+        flops=W.algorithmic_flops(p),
+        mfma_dtype="fp8" if (p.kv_dtype == W.KV_FP8_E4M3FN and p.qk_dim == 576) else "bf16",
     )
+    rec["mfma_tflops"] = rec["flops"] / (fwd_ms * 1e-3) / 1e12
     log(f"[bench] config {idx}: {ms_per_step * 1e3:.1f} us/step (bt {rec['bt_us']:.1f} + fwd "
         f"{rec['fwd_us']:.1f} + combine {rec['comb_us']:.1f} us), KV {kv_bytes / 1e6:.1f} MB, "
         f"step {rec['step_gbs']:.0f} GB/s, fwd {rec['fwd_gbs']:.0f} GB/s "
@@ -319,6 +325,14 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    def mfma_summary(r):
+        # algorithmic matrix flops of the split-KV pass over its event time, against the
+        # dense peak of the MFMA type the kernel runs
+        peak = MFMA_PEAK_TFLOPS[r["mfma_dtype"]]
+        return {"dtype": r["mfma_dtype"], "algorithmic_flops_per_launch": r["flops"],
+                "achieved_tflops": round(r["mfma_tflops"], 1), "peak_tflops": peak,
+                "frac": round(r["mfma_tflops"] / peak, 4)}
+
     def summary(r):
         return {
             "us_per_step": round(r["ms_per_step"] * 1e3, 2), "fwd_us": round(r["fwd_us"], 2),
@@ -331,6 +345,7 @@ def main():
             "call_pct_of_peak": round(100 * r["kv_bytes"] / (r["call_b2b_us"] * 1e-6)
                                       / 1e9 / HBM_PEAK_GBS, 2),
             "call_us_with_event_between": r["call_us"],
+            "mfma": mfma_summary(r),
             "splits": r["splits"], "kv_copies": r["copies"]}
 
     head = measure(args.config, args.steps, args.warmup, args.splits, log)
@@ -401,6 +416,8 @@ def main():
                       "combine": round(head["comb_us"], 2)},
         "event_gap_us": round(head["event_gap_us"], 2),
         "roofline": roof,
+        # the same kernel against the matrix cores (an HBM-bound kernel sits far below)
+        "mfma": mfma_summary(head),
         "cpu_baseline": cpu,
     }
     if per_config:

@@ -362,6 +362,16 @@ def algorithmic_kv_bytes(p: Problem) -> int:
                    for L, n in zip(p.prefix_lens, draft_rows(p)))) * per_tok
 
 
+def algorithmic_flops(p: Problem) -> int:
+    """Matrix flops of a verify call: every query row against every key its sequence
+    shows any row (the visible keys above), 2 (qk_dim + v_dim) flops per (row, key):
+    one multiply-add per element of QK^T and of PV.  Excludes the softmax and the
+    masked-out products inside partly visible tiles."""
+    per_row_key = 2 * (p.qk_dim + p.v_dim)
+    return int(sum(visible_token_count(int(L), n, p.window_left) * n * p.hq
+                   for L, n in zip(p.prefix_lens, draft_rows(p)))) * per_row_key
+
+
 def draft_rows(p: Problem):
     """Draft rows (and draft keys) of each sequence: D, or qo_indptr's counts."""
     if p.qo_indptr is None:
