@@ -119,6 +119,34 @@ void splitkv_tile_kernel(FwdParams P) {
   const bool rv = row < P.rows && row / P.group < seq_rows(P, b);
   const int row_i = rv ? row / P.group : 0;
   const bool tree = P.draft_slots != nullptr;
+  const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
+  // A slot lookup in two parts: lane_raw loads the page id of the lane's token of the
+  // block at t0 (its draft slot for tree-verify draft keys) with no branch, and
+  // lane_slot turns it into the slot where the value is used, so the wait for the
+  // load sits at the use.
+  auto lane_raw = [&](int t0) -> int {
+    const int t = min(t0 + (lane & (kTB - 1)), t_last);
+    const int32_t* src = (tree && t >= L) ? P.draft_slots + b * P.draft + (t - L) : bt_row + (t >> lg);
+    // a global (not flat) load: the compiler then waits for it by count and leaves
+    // the data loads issued after it in flight
+    return *(const __attribute__((address_space(1))) int32_t*)src;
+  };
+  auto lane_slot = [&](int raw, int t0) -> int {
+    const int t = min(t0 + (lane & (kTB - 1)), t_last);
+    return (tree && t >= L) ? raw : (raw << lg) | (t & pmask);
+  };
+  // Page ids: at step b (set s = b % kDepth), pid[s] holds block b + kDepth's and is
+  // refilled with block b + 2 kDepth's once used.  A lookup is issued kDepth steps
+  // before its use and each register is written and read once per kDepth steps, so
+  // the compiler's wait for a lookup leaves the later steps' data loads in flight.
+  // The piece's first lookups go out before anything else of its set-up: their round
+  // trip overlaps the q loads and row bounds below, and waiting for them never waits
+  // for q.
+  int first[kDepth], pid[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) first[u] = lane_raw(t_begin + u * kTB);
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) pid[u] = lane_raw(t_begin + (kDepth + u) * kTB);
   const uint32_t tbits = (tree && rv) ? tree_bits(P, b, row_i) : 0u;
 
   // Q^T operands of this wave's 16 rows: k-step ks holds elements 32ks + 8j + [0, 8)
@@ -155,22 +183,6 @@ void splitkv_tile_kernel(FwdParams P) {
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* bt_row = P.bt + (int64_t)b * P.max_pages;
-  // A slot lookup in two parts: lane_raw loads the page id of the lane's token of the
-  // block at t0 (its draft slot for tree-verify draft keys) with no branch, and
-  // lane_slot turns it into the slot where the value is used, so the wait for the
-  // load sits at the use.
-  auto lane_raw = [&](int t0) -> int {
-    const int t = min(t0 + (lane & (kTB - 1)), t_last);
-    const int32_t* src = (tree && t >= L) ? P.draft_slots + b * P.draft + (t - L) : bt_row + (t >> lg);
-    // a global (not flat) load: the compiler then waits for it by count and leaves
-    // the data loads issued after it in flight
-    return *(const __attribute__((address_space(1))) int32_t*)src;
-  };
-  auto lane_slot = [&](int raw, int t0) -> int {
-    const int t = min(t0 + (lane & (kTB - 1)), t_last);
-    return (tree && t >= L) ? raw : (raw << lg) | (t & pmask);
-  };
   // kDepth register sets: set s holds the blocks b with b % kDepth == s
   u32x4 kr[kDepth][G::NLD], vr[kDepth][G::NLD];
   // Slot s's row starts s * sslot bytes into the cache (the host checks that slot
@@ -209,17 +221,7 @@ void splitkv_tile_kernel(FwdParams P) {
   };
   using Sets = std::make_integer_sequence<int, kDepth>;
 
-  // Page ids: at step b (set s = b % kDepth), pid[s] holds block b + kDepth's and is
-  // refilled with block b + 2 kDepth's once used.  A lookup is issued kDepth steps
-  // before its use and each register is written and read once per kDepth steps, so
-  // the compiler's wait for a lookup leaves the later steps' data loads in flight.
-  int pid[kDepth];
   {
-    int first[kDepth];
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) first[u] = lane_raw(t_begin + u * kTB);
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) pid[u] = lane_raw(t_begin + (kDepth + u) * kTB);
     for_sets(
         [&](auto set) {
           constexpr int u = decltype(set)::value;

@@ -67,12 +67,19 @@ struct FwdParams {
   float logit_cap;             // > 0: natural-log scores s -> cap * tanh(s / cap)
 };
 
-// Draft rows of sequence b and the q/out row of its first one.
+// Read-only int32 tables (prefix lengths, row offsets, block table) through the constant address
+// space: a wave-uniform index then becomes a scalar load.
+__device__ __forceinline__ int load_ro(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// Draft rows of sequence b and the q/out row of its first one (scalar loads for a
+// uniform b: their waits never count the vector loads in flight).
 __device__ __forceinline__ int seq_rows(const FwdParams& P, int b) {
-  return P.qo_indptr ? P.qo_indptr[b + 1] - P.qo_indptr[b] : P.draft;
+  return P.qo_indptr ? load_ro(P.qo_indptr, b + 1) - load_ro(P.qo_indptr, b) : P.draft;
 }
 __device__ __forceinline__ int seq_row0(const FwdParams& P, int b) {
-  return P.qo_indptr ? P.qo_indptr[b] : b * P.draft;
+  return P.qo_indptr ? load_ro(P.qo_indptr, b) : b * P.draft;
 }
 
 // Slot of key t of sequence b: prefix keys (and, at topk = 1, draft keys) through
@@ -159,12 +166,6 @@ struct Piece {
   int count;   // on the sequence's last piece, its number of pieces; else 0
 };
 
-// Read-only int32 tables (prefix lengths, block table) through the constant address
-// space: a wave-uniform index then becomes a scalar load.
-__device__ __forceinline__ int load_ro(const int32_t* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
-
 __device__ __forceinline__ int seq_prefix_len(const FwdParams& P, int b) {
   return max(load_ro(P.prefix_lens, b), 0);
 }
@@ -189,6 +190,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 struct PieceWalk {
   int64_t a, e, q, cum;  // range [a, e) and sequence b's virtual start, in virtual keys
   int b, y, len;
+  int Lb;  // sequence b's prefix length when already loaded, else -1 (saves piece() a load)
 
   __device__ int keys_of(const FwdParams& P, int c) const {
     return seq_len_keys(P, c, seq_prefix_len(P, c));
@@ -202,12 +204,15 @@ struct PieceWalk {
     const int lane = threadIdx.x & 63;
     y = row;
     if (P.slots == 1) {
-      if (y >= P.batch || keys_of(P, y) == 0) return false;
+      if (y >= P.batch) return false;
+      Lb = seq_prefix_len(P, y);
+      if (seq_len_keys(P, y, Lb) == 0) return false;
       b = y;
       q = 0;
       return true;
     }
-    const int ln0 = lane < P.batch ? keys_of(P, lane) : 0;
+    const int L0 = lane < P.batch ? seq_prefix_len(P, lane) : 0;
+    const int ln0 = lane < P.batch ? seq_len_keys(P, lane, L0) : 0;
     int64_t T = 0;
     int mx = 0;
     for (int c = 0; c < P.batch; c += 64) {
@@ -258,6 +263,7 @@ struct PieceWalk {
       if (hit) {
         const int f = __builtin_ctzll(hit);
         b = c + f;
+        Lb = c == 0 ? __builtin_amdgcn_readlane(L0, f) : -1;
         cum = uniform64(base + __shfl(incl, f, 64) - __shfl(vl, f, 64));
         // a range that ends inside b's virtual keys holds no real key
         return cum + P.piece_cost < e;
@@ -270,7 +276,7 @@ struct PieceWalk {
   __device__ Piece piece(const FwdParams& P) {
     Piece pc;
     pc.b = __builtin_amdgcn_readfirstlane(b);
-    pc.L = __builtin_amdgcn_readfirstlane(seq_prefix_len(P, pc.b));
+    pc.L = __builtin_amdgcn_readfirstlane(Lb >= 0 ? Lb : seq_prefix_len(P, pc.b));
     const int lo = seq_lo(P, pc.L);
     len = seq_len_keys(P, pc.b, pc.L);
     if (P.slots == 1) {
@@ -302,7 +308,8 @@ struct PieceWalk {
     // the next sequence with keys (sequences without rows own none)
     while (cum < e && b + 1 < P.batch) {
       ++b;
-      len = keys_of(P, b);
+      Lb = seq_prefix_len(P, b);
+      len = seq_len_keys(P, b, Lb);
       if (len > 0) return cum + P.piece_cost < e;
     }
     return false;
