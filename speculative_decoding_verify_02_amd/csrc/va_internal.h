@@ -325,8 +325,8 @@ int launch_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int3
                        int lg_page, int32_t max_pages, int32_t* block_table, int32_t* kv_lens,
                        hipStream_t stream);
 int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t stream);
-// bf16 heads with qk_dim = v_dim in {128, 256}: whole-slot-row tiles shared by
-// hpc heads x nrg row groups.
+// bf16 heads with qk_dim = v_dim = 256: whole-slot-row tiles shared by hpc heads x
+// nrg row groups (hpc x nrg in 1x1, 2x1, 4x1, 1x2, 2x2, 1x4); other d is rejected.
 int launch_splitkv_tile(const FwdParams& fp, int d, int hpc, int nrg, dim3 grid, hipStream_t stream);
 // fp8 MLA heads (qk_dim 576, v_dim 512 = first 512 of the K row), <= 64 rows per head.
 int launch_splitkv_mla_fp8(const FwdParams& fp, const Plan& p, dim3 grid, hipStream_t stream);
