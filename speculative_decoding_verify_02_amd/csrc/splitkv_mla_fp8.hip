@@ -7,7 +7,8 @@
 //
 //   workgroup = (KV head g, key range y: pieces of sequences), 8 waves, two per
 //   SIMD.  Wave w = (row group rg = w % 4, half hf = w / 4): the pair (rg, 0),
-//   (rg, 1) shares query rows 16 rg .. 16 rg + 15, whose q both keep in registers.
+//   (rg, 1) shares query rows 16 rg .. 16 rg + 15, whose q both keep in registers
+//   (each loads and converts half of it and hands that half to the other).
 //   Per tile of 128 keys:
 //     QK  wave hf scores keys 64 hf .. 64 hf + 63 of the tile (S^T = K Q^T);
 //     the pair swaps row maxima through LDS, so both take the same running max,
@@ -210,17 +211,26 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
 
   // key of lane l < 16 among this wave's 16 copies of tile k (clamped to the piece)
   auto copy_key = [&](int k) { return min(t_begin + k * kMB + wave * kKPW + (lane & 15), t_last); };
+  // page id of that key, branch-free (a tree-verify draft key reads entry 0 and takes
+  // its draft slot in make_slot), so the compiler's waits count this load exactly
   auto load_pid = [&](int k) -> int {
     const int t = copy_key(k);
-    return (tree && t >= L) ? 0 : bt_row[t >> lg];
+    const bool draft_key = tree && t >= L;
+    const int v = *(const __attribute__((address_space(1))) int32_t*)(bt_row + (draft_key ? 0 : t >> lg));
+    return draft_key ? 0 : v;
   };
-  // The slot may come from a load (tree verify): the empty asm consumes it here, so
-  // the compiler's wait for that load sits before the copies, never after them.
+  // The draft slot of a tree-verify key is one more load: the empty asm takes its
+  // wait inside the (uniform) tree branch, before the copies; the plain path waits
+  // only for the page id.
   auto make_slot = [&](int pid, int k) -> int {
     const int t = copy_key(k);
-    int slot = (tree && t >= L) ? P.draft_slots[b * P.draft + (t - L)]  // tree verify draft keys
-                                : (pid << lg) | (t & pmask);
-    asm volatile("" : "+v"(slot));
+    int slot = (pid << lg) | (t & pmask);
+    if (tree) {
+      int s = *(const __attribute__((address_space(1))) int32_t*)(
+          P.draft_slots + b * P.draft + min(max(t - L, 0), P.draft - 1));
+      asm volatile("" : "+v"(s));
+      slot = t >= L ? s : slot;
+    }
     return slot;
   };
   // latent bytes of keys 2i, 2i+1 of this wave's 16 keys of tile k -> ring buffer
@@ -251,48 +261,53 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
   // bf16 q itself), the 64-wide rope tail d >= 512 as bf16.  Lane group j holds
   // elements 128kb + 32j + [0, 32) (and 512 + 32h + 8j + [0, 8) of the tail), the
   // k-slots of the K operand read below.
-  // The loads (q, page ids of tiles 0 and 1) are issued before the copies of tile 0,
-  // and q is converted while those copies are in flight.
+  // Each wave of the pair loads and converts half of the latent q (blocks kb = 2 hf,
+  // 2 hf + 1) and hands it to the other through ring buffer 1, which tile 1 fills
+  // only later.  The page ids of tiles 0 and 1 are loaded first, so the copies of
+  // tile 0 wait only for them and are in flight together with q.
   i32x8 qh[kLat / 128], ql[kLat / 128];
   u32x4 qr[2];
   {
+    // rows past the sequence's count read q row 0 (always present) and are zeroed
     const int hh = rv ? row % P.group : 0;
-    const uint8_t* qp =
-        P.q + (int64_t)(seq_row0(P, b) + row_i) * P.q_srow + (int64_t)(g * P.group + hh) * P.q_shead;
-    u32x4 raw[kLat / 128][4];
+    const uint8_t* qp = rv ? P.q + (int64_t)(seq_row0(P, b) + row_i) * P.q_srow +
+                                 (int64_t)(g * P.group + hh) * P.q_shead
+                           : P.q;
+    const int pid0 = load_pid(0);
+    pid = load_pid(1);
+    u32x4 raw[2][4];
 #pragma unroll
-    for (int kb = 0; kb < kLat / 128; ++kb)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        raw[kb][c] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (128 * kb + 32 * j + 8 * c))
-                        : u32x4{0u, 0u, 0u, 0u};
+        raw[kk][c] = *reinterpret_cast<const u32x4*>(qp + 2 * (128 * (2 * hf + kk) + 32 * j + 8 * c));
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      qr[h] = rv ? *reinterpret_cast<const u32x4*>(qp + 2 * (kLat + 32 * h + 8 * j))
-                 : u32x4{0u, 0u, 0u, 0u};
-    int pid0 = load_pid(0);
-    if (ntile > 1) pid = load_pid(1);
+    for (int h = 0; h < 2; ++h) qr[h] = *reinterpret_cast<const u32x4*>(qp + 2 * (kLat + 32 * h + 8 * j));
     slot_nx = make_slot(pid0, 0);
-    // q has landed (it was loaded before the page ids); the empty asm makes the
-    // compiler take that wait here, not after the copies
-#pragma unroll
-    for (int kb = 0; kb < kLat / 128; ++kb)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(raw[kb][c]));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(qr[h]));
 #pragma unroll
     for (int i = 0; i < kKPW / 2; ++i) copy_pair(0, slot_nx, i);
     copy_rope(slot_nx);
+    // the conversion stays after the copies (its wait for q then counts them too)
 #pragma unroll
-    for (int kb = 0; kb < kLat / 128; ++kb) {
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(raw[kk][c]));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(qr[h]));
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qr[h] = rv ? qr[h] : zero;
+    i32x8 oh[2], ol[2];  // this wave's half
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        const u32x4 r = rv ? raw[kk][c] : zero;
         float x[8];  // q elements, saturated to the e4m3 range (+-448)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = fminf(fmaxf(__uint_as_float(raw[kb][c][e] << 16), -448.f), 448.f);
-          x[2 * e + 1] = fminf(fmaxf(__uint_as_float(raw[kb][c][e] & 0xffff0000u), -448.f), 448.f);
+          x[2 * e] = fminf(fmaxf(__uint_as_float(r[e] << 16), -448.f), 448.f);
+          x[2 * e + 1] = fminf(fmaxf(__uint_as_float(r[e] & 0xffff0000u), -448.f), 448.f);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -304,10 +319,44 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
                                                    (x[4 * h + 1] - a[1]) * 16.f, 0, false);
           wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h + 2] - c2[0]) * 16.f,
                                                (x[4 * h + 3] - c2[1]) * 16.f, wl, true);
-          qh[kb][2 * c + h] = w;
-          ql[kb][2 * c + h] = wl;
+          oh[kk][2 * c + h] = w;
+          ol[kk][2 * c + h] = wl;
         }
       }
+    }
+    // Exchange through ring buffer 1: 16-byte chunk i of lane l at 1024 i + 16 l of
+    // the 8 KB that the partner's copies of tile 1 fill (its keys 16 partner ..
+    // 16 partner + 15).  Each wave reads its own region and waits for the reads
+    // before its first copy of tile 1 overwrites it.
+    auto chunk = [&](const i32x8* v, int i) {
+      const i32x8 x = v[i >> 1];
+      return (i & 1) ? i32x4{x[4], x[5], x[6], x[7]} : i32x4{x[0], x[1], x[2], x[3]};
+    };
+    uint8_t* xo = s_lat[1] + 8192 * partner + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<i32x4*>(xo + 1024 * i) = chunk(oh, i);
+      *reinterpret_cast<i32x4*>(xo + 1024 * (4 + i)) = chunk(ol, i);
+    }
+    lds_barrier();
+    const uint8_t* xi = s_lat[1] + 8192 * wave + 16 * lane;
+    i32x4 ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = *reinterpret_cast<const i32x4*>(xi + 1024 * i);
+      pl[i] = *reinterpret_cast<const i32x4*>(xi + 1024 * (4 + i));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const i32x8 th = {ph[2 * kk][0], ph[2 * kk][1], ph[2 * kk][2], ph[2 * kk][3],
+                        ph[2 * kk + 1][0], ph[2 * kk + 1][1], ph[2 * kk + 1][2], ph[2 * kk + 1][3]};
+      const i32x8 tl = {pl[2 * kk][0], pl[2 * kk][1], pl[2 * kk][2], pl[2 * kk][3],
+                        pl[2 * kk + 1][0], pl[2 * kk + 1][1], pl[2 * kk + 1][2], pl[2 * kk + 1][3]};
+      qh[kk] = hf ? th : oh[kk];
+      ql[kk] = hf ? tl : ol[kk];
+      qh[2 + kk] = hf ? oh[kk] : th;
+      ql[2 + kk] = hf ? ol[kk] : tl;
     }
   }
 
@@ -325,7 +374,7 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
     // them then never counts the copies still in flight
     const bool next = k + 1 < ntile;
     if (next) slot_nx = make_slot(pid, k + 1);
-    if (k + 2 < ntile) pid = load_pid(k + 2);
+    pid = load_pid(k + 2);  // clamped to the piece's last key past its end
 
     const int t0 = t_begin + k * kMB;
     const int th = t0 + 64 * hf;  // first key this wave scores
