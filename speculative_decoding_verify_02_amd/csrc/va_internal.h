@@ -187,6 +187,76 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Wave-wide (64-lane) reductions and scan on VALU lane moves instead of LDS permutes:
+// DPP inside a 16-lane row (quad xor 1 / xor 2, half-row and row mirror, row shift
+// right, broadcast of lanes 15 and 31 into the following rows) and gfx950's row swaps
+// across rows.  The control words are the GFX9 DPP encodings.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ int64_t make64(uint32_t lo, uint32_t hi) {
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// lane moved by DPP control C, rows outside row_mask keep 0, sources outside the row read 0
+template <int C, int RowMask = 0xf>
+__device__ __forceinline__ int64_t dpp64(int64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(uint64_t)x, C, RowMask, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)x >> 32), C, RowMask, 0xf, true);
+  return make64((uint32_t)lo, (uint32_t)hi);
+}
+template <int C>
+__device__ __forceinline__ int dpp32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, C, 0xf, 0xf, true);
+}
+// sum over all 64 lanes, in every lane
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+  x += dpp64<kDppQuadXor1>(x);
+  x += dpp64<kDppQuadXor2>(x);
+  x += dpp64<kDppRowHalfMirror>(x);
+  x += dpp64<kDppRowMirror>(x);
+  // rows 2r and 2r+1, then the two halves: each lane gets both values of the swap
+  const uint32_t lo = (uint32_t)(uint64_t)x, hi = (uint32_t)((uint64_t)x >> 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  x = make64(a[0], c[0]) + make64(a[1], c[1]);
+  const uint32_t lo2 = (uint32_t)(uint64_t)x, hi2 = (uint32_t)((uint64_t)x >> 32);
+  const auto d = __builtin_amdgcn_permlane32_swap(lo2, lo2, false, false);
+  const auto f = __builtin_amdgcn_permlane32_swap(hi2, hi2, false, false);
+  return make64(d[0], f[0]) + make64(d[1], f[1]);
+}
+// max over all 64 lanes, in every lane
+__device__ __forceinline__ int wave_max32(int x) {
+  x = max(x, dpp32<kDppQuadXor1>(x));
+  x = max(x, dpp32<kDppQuadXor2>(x));
+  x = max(x, dpp32<kDppRowHalfMirror>(x));
+  x = max(x, dpp32<kDppRowMirror>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = max((int)a[0], (int)a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return max((int)c[0], (int)c[1]);
+}
+// inclusive prefix sum over lanes 0..63
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x) {
+  x += dpp64<kDppRowShr1>(x);
+  x += dpp64<kDppRowShr2>(x);
+  x += dpp64<kDppRowShr4>(x);
+  x += dpp64<kDppRowShr8>(x);
+  x += dpp64<kDppRowBcast15, 0xa>(x);  // rows 1, 3 add the last lane of rows 0, 2
+  x += dpp64<kDppRowBcast31, 0xc>(x);  // rows 2, 3 add lane 31
+  return x;
+}
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l) {
+  return make64(__builtin_amdgcn_readlane((uint32_t)(uint64_t)x, l),
+                __builtin_amdgcn_readlane((uint32_t)((uint64_t)x >> 32), l));
+}
+// a / b for 0 <= a, 0 < b, both wave-uniform: 32-bit division when both fit
+__device__ __forceinline__ int64_t udiv64(int64_t a, int64_t b) {
+  if ((uint64_t)(a | b) <= 0xffffffffull) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 struct PieceWalk {
   int64_t a, e, q, cum;  // range [a, e) and sequence b's virtual start, in virtual keys
   int b, y, len;
@@ -222,21 +292,14 @@ struct PieceWalk {
       } else if (c + lane < P.batch) {
         l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
       }
-      int64_t sum = vlen(P, l);
-      int m = l;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        sum += __shfl_xor(sum, off, 64);
-        m = max(m, __shfl_xor(m, off, 64));
-      }
-      T += sum;
-      mx = max(mx, m);
+      T += wave_sum64(vlen(P, l));
+      mx = max(mx, wave_max32(l));
     }
     T = uniform64(T);
     mx = __builtin_amdgcn_readfirstlane(mx);
     const int nwy = gridDim.y;
-    int64_t qq = (T + nwy - 1) / nwy;
-    const int64_t qs = ((int64_t)mx + P.slots - 2) / (P.slots - 1);
+    int64_t qq = udiv64(T + nwy - 1, nwy);
+    const int64_t qs = udiv64((int64_t)mx + P.slots - 2, P.slots - 1);
     if (qs > qq) qq = qs;
     if (qq < P.min_q) qq = P.min_q;
     q = qq;
@@ -253,22 +316,17 @@ struct PieceWalk {
         l = seq_len_keys(P, c + lane, seq_prefix_len(P, c + lane));
       }
       const int64_t vl = vlen(P, l);
-      int64_t incl = vl;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int64_t t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-      }
+      const int64_t incl = wave_incl_scan64(vl);
       const uint64_t hit = __ballot(base + incl > a);
       if (hit) {
         const int f = __builtin_ctzll(hit);
         b = c + f;
         Lb = c == 0 ? __builtin_amdgcn_readlane(L0, f) : -1;
-        cum = uniform64(base + __shfl(incl, f, 64) - __shfl(vl, f, 64));
+        cum = uniform64(base + readlane64(incl, f) - readlane64(vl, f));
         // a range that ends inside b's virtual keys holds no real key
         return cum + P.piece_cost < e;
       }
-      base += __shfl(incl, 63, 64);
+      base += readlane64(incl, 63);
     }
     return false;  // unreachable for a < T
   }
@@ -291,7 +349,7 @@ struct PieceWalk {
     const int64_t s1 = e < sb + len ? e : sb + len;
     pc.t0 = lo + (int)(s0 - sb);
     pc.t1 = lo + (int)(s1 - sb);
-    const int64_t first = sb / q, last = (sb + len - 1) / q;
+    const int64_t first = udiv64(sb, q), last = udiv64(sb + len - 1, q);
     pc.slot = (int)(y - first);
     pc.count = (y == last) ? (int)(last - first + 1) : 0;
     pc.t0 = __builtin_amdgcn_readfirstlane(pc.t0);
