@@ -142,6 +142,21 @@ def test_partition_many_short_sequences(window):
     check(p, num_splits=1)
 
 
+@pytest.mark.parametrize("dims", [1, 2])
+def test_partition_many_short_sequences_wide_heads(dims):
+    # the d = 256 tile kernel and the fp8 MLA kernel walking many pieces per workgroup:
+    # every piece after the first redoes the q load (for MLA, the pair's hand-off of q
+    # halves through the free ring buffer) after the previous piece's last tile.  One long
+    # sequence with two slots makes each workgroup's range as long as it, so the ranges
+    # that follow it span dozens of the short sequences.
+    hq, hkv = (16, 1) if dims == 2 else (8, 2)
+    lens = [6000] + [int(x) for x in np.random.default_rng(350 + dims).integers(0, 60, size=99)]
+    p = W.make_problem(name="many-wide", batch=len(lens), prefix_lens=lens, hq=hq, hkv=hkv,
+                       page_size=4, seed=340 + dims, **DIMS[dims])
+    check(p, num_splits=2)
+    check(p)
+
+
 @pytest.mark.parametrize("window", [0, 1, 3, 4, 17, 256, 5000])
 @pytest.mark.parametrize("dims", [0, 1, 2])
 def test_windows(window, dims):
