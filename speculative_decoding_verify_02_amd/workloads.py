@@ -210,8 +210,10 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
         nq = np.random.default_rng(kids[4]).integers(1, draft_len + 1, size=batch).astype(np.int64)
     else:
         nq = np.full(batch, draft_len, dtype=np.int64)
-    if (ragged or draft_counts is not None) and ((nq < 1).any() or (nq > draft_len).any()):
-        raise ValueError("draft counts must be in [1, draft_len]")
+    # explicit counts may hold 0 (a sequence with no rows owns no keys this call);
+    # random ragged counts are in [1, draft_len]
+    if (ragged or draft_counts is not None) and ((nq < 0).any() or (nq > draft_len).any()):
+        raise ValueError("draft counts must be in [0, draft_len]")
     # token list: prefix then the sequence's draft tokens (tree: prefix only)
     n_tok = lens if tree else lens + nq
     n_pages = -(-n_tok // page_size)

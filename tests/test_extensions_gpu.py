@@ -32,6 +32,16 @@ def test_ragged_rows_explicit_counts_and_window():
     check(p, num_splits=1)
 
 
+@pytest.mark.parametrize("dims", [0, 1, 2])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_ragged_rows_with_empty_sequences(dims, splits):
+    # qo_indptr may repeat an entry: those sequences have no rows and own no keys, so
+    # the partition skips them and the combine has nothing of theirs to merge
+    p = _problem(dims, 730 + dims, prefix_lens=[300, 0, 700, 65, 1, 50, 129],
+                 draft_counts=[0, 4, 0, 2, 1, 0, 3], batch=7)
+    check(p, num_splits=splits or None)
+
+
 @pytest.mark.parametrize("dims", [0, 1, 2, 3])
 @pytest.mark.parametrize("splits", [0, 2])
 def test_tree_verify(dims, splits):
