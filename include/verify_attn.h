@@ -34,7 +34,8 @@
  *     so calls are safe to record into a HIP graph (workspace addresses stay fixed).
  *   - Calls return a status; on any status other than VA_OK nothing was launched.
  *     Device data that breaks a stated precondition (page ids outside the pool,
- *     a block table too narrow) is NOT detected and may fault the GPU.
+ *     a block table too narrow) is NOT detected and may fault the GPU (the Python
+ *     binding has an optional host-side validator for integration and debugging).
  *   - Indices are int32; byte offsets are computed in 64 bits.
  */
 #ifndef VERIFY_ATTN_H
@@ -90,7 +91,7 @@ typedef struct verify_attn_args {
                                workgroup, and S bounds how many ranges one sequence
                                may span (1 = one workgroup per sequence).           */
 
-    /* q: [B*D, hq, qk_dim] bf16                                                        */
+    /* q: [B*D, hq, qk_dim] bf16, any finite values                                     */
     const void* q;
     int64_t q_stride_row, q_stride_head;
     /* K cache: row of token slot s, KV head g at k_cache + s*k_stride_slot +
@@ -101,7 +102,8 @@ typedef struct verify_attn_args {
     const void* k_cache;
     int64_t k_stride_slot, k_stride_head;
     /* V cache, same addressing, v_dim elements.  May equal k_cache with the same
-       strides (MLA: V is the first v_dim columns of the K row).                        */
+       strides (MLA: V is the first v_dim columns of the K row); fp8 576/512 calls
+       whose V is that view take the latent-head kernel, others the generic one.       */
     const void* v_cache;
     int64_t v_stride_slot, v_stride_head;
     /* [B, max_pages_per_seq] int32 page ids, from verify_attn_build_block_table       */
@@ -206,10 +208,16 @@ int verify_attn_can_handle(const verify_attn_args* args);
 
 /*
  * Split slots per (sequence, KV head) that the heuristic picks for these arguments
- * on the current device (from its compute-unit count and the kernel the arguments
- * select); args->num_splits is ignored.  Host only, reads no device memory: the
- * pointers may still be unset.  Returns >= 1, or -1 when the arguments are rejected
- * (the status verify_attn_can_handle would give).
+ * on the current device: how many programs the long shared prefix may be spread
+ * over (PR #27382, "Motivation": split the prefix across parallel programs), from
+ * the compute-unit count and the kernel the arguments select; args->num_splits is
+ * ignored.  It takes the whole argument struct rather than a list of scalars because
+ * the choice depends on every field the gate reads (KV dtype, qk_dim and v_dim, the
+ * window, GQA ratio and draft length pick the kernel, and the kernel sets the tile
+ * and per-piece cost).  Size the workspace with it once for the largest batch and
+ * keep it (PR #27382 review: scratch keyed on a stable max batch).  Host only,
+ * reads no device memory: the pointers may still be unset.  Returns >= 1, or -1
+ * when the arguments are rejected (the status verify_attn_can_handle would give).
  */
 int32_t verify_attn_num_splits(const verify_attn_args* args);
 

@@ -4,7 +4,9 @@ Every step of the verify path runs in the library's HIP kernels; this module
 turns torch tensors into the pointers, strides and scalars the C ABI of
 ``include/verify_attn.h`` takes.  PyTorch provides device memory and the
 current stream, nothing else.  If the library is missing the functions raise:
-there is no CPU or PyTorch fallback.
+there is no CPU or PyTorch fallback.  An optional host-side validator (off by
+default, ``set_debug_validation``) checks the device data the kernels trust
+before a launch.
 """
 
 from __future__ import annotations
@@ -83,6 +85,29 @@ class VerifyAttnArgs(ctypes.Structure):
 V1_SIZE = VerifyAttnArgs.qo_indptr.offset
 
 
+class VerifyAttnInputError(ValueError):
+    """A precondition of include/verify_attn.h that the kernels trust is broken (raised by
+    the optional host-side validator before anything is launched)."""
+
+
+# Host-side debug validation of the device inputs the kernels trust (page ids inside the
+# pool, consecutive slots within a page, block-table width, row offsets).  Off by
+# default: it copies those tensors to the host and synchronises.  A bad page id is a GPU
+# memory fault, not a status code (the unified-attention page splits HSA memory-access
+# faults out as their own fix), so a caller can switch this on while integrating.
+_debug_validate = os.environ.get("VERIFY_ATTN_DEBUG_VALIDATE", "0") == "1"
+
+
+def set_debug_validation(on: bool) -> None:
+    """Switch the host-side validator for build_block_table / fwd / combine on or off."""
+    global _debug_validate
+    _debug_validate = bool(on)
+
+
+def debug_validation() -> bool:
+    return _debug_validate
+
+
 class VerifyAttnError(RuntimeError):
     def __init__(self, func: str, status: int, text: str):
         super().__init__(f"{func} failed with status {status} ({text})")
@@ -150,13 +175,129 @@ def _ptr(t) -> Optional[int]:
 # a1: block table
 # ---------------------------------------------------------------------------
 
+def _host(t):
+    import numpy as np
+    return None if t is None else np.asarray(t.detach().cpu().numpy())
+
+
+def validate_block_table_inputs(kv_indptr, kv_indices, page_size: int, max_pages_per_seq: int,
+                                num_slots: Optional[int] = None) -> None:
+    """Host check of verify_attn_build_block_table's preconditions (NumPy arrays or
+    tensors): kv_indptr starts at 0 and never decreases, kv_indices holds its entries,
+    every slot lies in the pool, each sequence starts at offset 0 of a page and the
+    slots of one page are consecutive (true at topk = 1, the page-size page's review),
+    and no sequence needs more pages than the table is wide.  Raises
+    VerifyAttnInputError naming the first violation."""
+    import numpy as np
+    ind = np.asarray(_host(kv_indptr) if hasattr(kv_indptr, "cpu") else kv_indptr, dtype=np.int64)
+    idx = np.asarray(_host(kv_indices) if hasattr(kv_indices, "cpu") else kv_indices,
+                     dtype=np.int64)
+    if ind.ndim != 1 or ind.size < 1:
+        raise VerifyAttnInputError("kv_indptr must be a 1-D array of batch + 1 entries")
+    if ind[0] != 0:
+        raise VerifyAttnInputError(f"kv_indptr[0] = {ind[0]}, must be 0")
+    n = np.diff(ind)
+    if (n < 0).any():
+        b = int(np.argmax(n < 0))
+        raise VerifyAttnInputError(f"kv_indptr decreases at sequence {b}")
+    if ind[-1] > idx.size:
+        raise VerifyAttnInputError(f"kv_indptr[B] = {ind[-1]} exceeds the {idx.size} kv_indices")
+    used = idx[:ind[-1]]
+    if used.size and (used.min() < 0 or (num_slots is not None and used.max() >= num_slots)):
+        raise VerifyAttnInputError(f"a slot in kv_indices lies outside the pool of {num_slots} slots")
+    pages = -(-n // page_size)
+    if pages.size and pages.max() > max_pages_per_seq:
+        b = int(np.argmax(pages))
+        raise VerifyAttnInputError(f"sequence {b} needs {pages[b]} pages, the table has "
+                                   f"{max_pages_per_seq} columns")
+    for b in range(n.size):
+        s = idx[ind[b]:ind[b + 1]]
+        t = np.arange(s.size)
+        if (s % page_size != t % page_size).any():
+            raise VerifyAttnInputError(f"sequence {b}: a token's slot is not at its offset in a "
+                                       f"page (sequences start at offset 0 of a page)")
+        first = s[t - t % page_size]
+        if (s != first + t % page_size).any():
+            raise VerifyAttnInputError(f"sequence {b}: the slots of one page are not consecutive")
+
+
+def validate_call(call: "VerifyCall", kv_indptr=None) -> None:
+    """Host check of the device data verify_attn_fwd and verify_attn_combine trust: prefix
+    lengths >= 0, ragged row offsets (from 0, non-decreasing, at most draft_len rows per
+    sequence, within q), block-table columns enough for every sequence's keys, page ids
+    of those columns inside the K and V pools, tree-verify draft slots inside the pools,
+    and (when the token-level kv_indptr the table came from is given) that sequence b
+    holds L_b + n_b tokens (L_b at tree verify).  Raises VerifyAttnInputError."""
+    import numpy as np
+    a, t = call.args, call.tensors
+    B, D, P = a.batch, a.draft_len, a.page_size
+    if B == 0:
+        return
+    L = np.asarray(_host(t["prefix_lens"]), dtype=np.int64).reshape(-1)
+    if L.size != B:
+        raise VerifyAttnInputError(f"prefix_lens has {L.size} entries for batch {B}")
+    if (L < 0).any():
+        raise VerifyAttnInputError(f"prefix_lens[{int(np.argmax(L < 0))}] is negative")
+    q_rows = t["q"].shape[0]
+    if t.get("qo_indptr") is not None:
+        qo = np.asarray(_host(t["qo_indptr"]), dtype=np.int64).reshape(-1)
+        if qo.size != B + 1 or qo[0] != 0:
+            raise VerifyAttnInputError("qo_indptr must hold batch + 1 offsets starting at 0")
+        nr = np.diff(qo)
+        if (nr < 0).any() or (nr > D).any():
+            raise VerifyAttnInputError("qo_indptr must not decrease and gives at most draft_len "
+                                       "rows per sequence")
+        if qo[-1] > q_rows:
+            raise VerifyAttnInputError(f"qo_indptr[B] = {qo[-1]} exceeds the {q_rows} rows of q")
+    else:
+        nr = np.full(B, D, dtype=np.int64)
+        if B * D > q_rows:
+            raise VerifyAttnInputError(f"q has {q_rows} rows, batch x draft_len = {B * D}")
+    tree = t.get("draft_slots") is not None
+    keys = L if tree else L + nr
+    keys = np.where(nr > 0, keys, 0)   # a sequence without rows reads nothing
+    bt = np.asarray(_host(t["block_table"]), dtype=np.int64)
+    if bt.ndim != 2 or bt.shape[0] < B or bt.shape[1] != a.max_pages_per_seq:
+        raise VerifyAttnInputError("block_table must be [batch, max_pages_per_seq]")
+    pages = -(-keys // P)
+    if pages.max() > a.max_pages_per_seq:
+        b = int(np.argmax(pages))
+        raise VerifyAttnInputError(f"sequence {b} needs {pages[b]} pages, the table has "
+                                   f"{a.max_pages_per_seq} columns")
+    k_slots = t["k_cache"].shape[0]
+    v_slots = t["v_cache"].shape[0]
+    pool_pages = min(k_slots, v_slots) // P
+    for b in range(B):
+        ids = bt[b, :pages[b]]
+        if ids.size and (ids.min() < 0 or ids.max() >= pool_pages):
+            raise VerifyAttnInputError(f"sequence {b}: a page id in the block table lies outside "
+                                       f"the pool of {pool_pages} pages")
+    if tree:
+        ds = np.asarray(_host(t["draft_slots"]), dtype=np.int64)
+        if ds.size < B * D or ds[:B * D].min() < 0 or ds[:B * D].max() >= min(k_slots, v_slots):
+            raise VerifyAttnInputError("draft_slots must hold [batch, draft_len] slots inside the pool")
+    if kv_indptr is not None:
+        ind = np.asarray(_host(kv_indptr) if hasattr(kv_indptr, "cpu") else kv_indptr,
+                         dtype=np.int64).reshape(-1)
+        if ind.size != B + 1:
+            raise VerifyAttnInputError(f"kv_indptr has {ind.size} entries for batch {B}")
+        bad = (nr > 0) & (np.diff(ind) != keys)
+        if bad.any():
+            b = int(np.argmax(bad))
+            raise VerifyAttnInputError(f"sequence {b}: kv_indptr gives {int(ind[b + 1] - ind[b])} "
+                                       f"tokens, prefix_lens and the draft rows give {keys[b]}")
+
+
 def verify_attn_build_block_table(kv_indptr, kv_indices, page_size: int, max_pages_per_seq: int,
                                   block_table=None, kv_lens=None, stream=None, check=True):
     """Scatter token-level slots into a [B, max_pages] int32 page table (on the GPU).
 
     ``kv_indptr`` [B+1] and ``kv_indices`` int32 CUDA tensors.  Allocates the outputs
-    when not given.  Returns (block_table, kv_lens) or the raw status if check=False."""
+    when not given.  Returns (block_table, kv_lens) or the raw status if check=False.
+    With debug validation on, the inputs are checked on the host first."""
     import torch
+    if _debug_validate:
+        validate_block_table_inputs(kv_indptr, kv_indices, page_size, max_pages_per_seq)
     batch = kv_indptr.numel() - 1
     dev = kv_indptr.device
     if block_table is None:
@@ -246,6 +387,8 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
 
 
 def verify_attn_fwd(call: VerifyCall, stream=None, check=True) -> int:
+    if _debug_validate:
+        validate_call(call)
     st = load().verify_attn_fwd(ctypes.byref(call.args), _stream_ptr(stream))
     if check:
         _check("verify_attn_fwd", st)
@@ -253,6 +396,8 @@ def verify_attn_fwd(call: VerifyCall, stream=None, check=True) -> int:
 
 
 def verify_attn_combine(call: VerifyCall, stream=None, check=True) -> int:
+    if _debug_validate:
+        validate_call(call)
     st = load().verify_attn_combine(ctypes.byref(call.args), _stream_ptr(stream))
     if check:
         _check("verify_attn_combine", st)

@@ -33,12 +33,13 @@
 //   rows {0..7, 16..23} (or {8..15, 24..31}) of a transposed read fall on distinct
 //   banks.  Rope row t sits at 64 t with chunk c stored at c ^ ((t / 4) % 4).
 //
-//   QK: for d < 512 v_mfma_scale_f32_16x16x128_f8f6f4 with the K bytes as they are
-//       and the bf16 q as two e4m3 terms hi + lo/16 (the lo product is scaled by
-//       2^-4 through the MFMA's MX block scale), ~2^-9 relative error in q, the
-//       precision bf16 itself carries.  The rope tail d in [512, 576) uses
-//       v_mfma_f32_16x16x32_bf16 with K widened exactly to bf16 (every e4m3fn
-//       value is a bf16 value) and q in bf16.
+//   QK: for d < 512 v_mfma_f32_16x16x128_f8f6f4 with the K bytes as they are and
+//       the bf16 q, scaled per row into [128, 256) by a power of two, as two e4m3
+//       terms hi + lo (~2^-9 of the row's largest magnitude, the precision bf16
+//       itself carries, for any finite q); the scores take the power of two back
+//       with sm_scale.  The rope tail d in
+//       [512, 576) uses v_mfma_f32_16x16x32_bf16 with K widened exactly to bf16
+//       (every e4m3fn value is a bf16 value) and q in bf16.
 //   softmax: online, exp2 domain.  The running max moves only when a score passes
 //       it by more than one (log2 units), so p <= 2 and most tiles skip rescaling
 //       the accumulator.
@@ -128,6 +129,7 @@ __shared__ __attribute__((aligned(128))) uint8_t s_lat[2][kLatTile];
 __shared__ __attribute__((aligned(128))) uint8_t s_rope[kRopeTile];
 __shared__ __attribute__((aligned(16))) i32x4 s_xp[kNW][2][64];
 __shared__ float s_xm[kNW][16];
+__shared__ uint32_t s_qex[4][16];  // per row group: the bf16 exponent field E of each q row
 
 }  // namespace
 
@@ -256,31 +258,43 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
   };
 
   int pid = 0, slot_nx = 0;
-  // this pair's 16 q rows in registers: for d < 512 as two e4m3 terms (hi = e4m3(q),
-  // lo = e4m3(16 (q - hi)), together ~2^-9 relative error, the precision of the
-  // bf16 q itself), the 64-wide rope tail d >= 512 as bf16.  Lane group j holds
-  // elements 128kb + 32j + [0, 32) (and 512 + 32h + 8j + [0, 8) of the tail), the
-  // k-slots of the K operand read below.
-  // Each wave of the pair loads and converts half of the latent q (blocks kb = 2 hf,
-  // 2 hf + 1) and hands it to the other through ring buffer 1, which tile 1 fills
-  // only later.  The page ids of tiles 0 and 1 are loaded first, so the copies of
-  // tile 0 wait only for them and are in flight together with q.
+  // This pair's 16 q rows in registers, scaled per row by 2^(134 - E) with E the bf16
+  // exponent field of the row's largest magnitude (latent and rope, at least 8), which
+  // puts that magnitude in [128, 256) whatever the range of q; the scores are scaled
+  // back by 2^(E - 134) with sm_scale.  For d < 512 the scaled q x is held as two e4m3
+  // terms, hi = e4m3(x) and lo = e4m3(x - hi): hi is off by at most 8 near the row's
+  // largest elements, where lo is a normal e4m3 number, so the pair carries ~2^-9 of
+  // the row's largest magnitude, the precision of the bf16 q itself.  The 64-wide
+  // rope tail d >= 512 stays bf16 (scaled exactly).  Lane group j holds elements
+  // 128kb + 32j + [0, 32) (and 512 + 32h + 8j + [0, 8) of the tail), the k-slots of
+  // the K operand read below.
+  // Each wave of the pair loads and converts 8 of the 16 rows (lane l: row
+  // 8 hf + l % 8, elements 64 (l / 8) + [0, 64) and 8 rope elements), so the row's
+  // exponent is found inside the wave, and hands the terms to both waves through ring
+  // buffer 1, which tile 1 fills only later.  The page ids of tiles 0 and 1 are loaded
+  // first, so the copies of tile 0 wait only for them and are in flight together with q.
   i32x8 qh[kLat / 128], ql[kLat / 128];
   u32x4 qr[2];
+  float c_row;  // sm_scale * k_scale * log2(e) * 2^(E - 134) of the lane's row
   {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
     // rows past the sequence's count read q row 0 (always present) and are zeroed
-    const int hh = rv ? row % P.group : 0;
-    const uint8_t* qp = rv ? P.q + (int64_t)(seq_row0(P, b) + row_i) * P.q_srow +
-                                 (int64_t)(g * P.group + hh) * P.q_shead
-                           : P.q;
+    auto q_row = [&](int r, bool ok) -> const uint8_t* {
+      return ok ? P.q + (int64_t)(seq_row0(P, b) + r / P.group) * P.q_srow +
+                      (int64_t)(g * P.group + r % P.group) * P.q_shead
+                : P.q;
+    };
+    const int crow = rg * 16 + 8 * hf + (lane & 7);  // the row this lane converts
+    const int cc = lane >> 3;                         // its 64-element chunk
+    const bool cv = crow < P.rows && crow / P.group < seq_rows(P, b);
+    const uint8_t* qc = q_row(crow, cv);
+    const uint8_t* qp = q_row(row, rv);
     const int pid0 = load_pid(0);
     pid = load_pid(1);
-    u32x4 raw[2][4];
+    u32x4 raw[9];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        raw[kk][c] = *reinterpret_cast<const u32x4*>(qp + 2 * (128 * (2 * hf + kk) + 32 * j + 8 * c));
+    for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(qc + 2 * (64 * cc + 8 * i));
+    raw[8] = *reinterpret_cast<const u32x4*>(qc + 2 * (kLat + 8 * cc));
 #pragma unroll
     for (int h = 0; h < 2; ++h) qr[h] = *reinterpret_cast<const u32x4*>(qp + 2 * (kLat + 32 * h + 8 * j));
     slot_nx = make_slot(pid0, 0);
@@ -289,25 +303,39 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
     copy_rope(slot_nx);
     // the conversion stays after the copies (its wait for q then counts them too)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(raw[kk][c]));
+    for (int i = 0; i < 9; ++i) asm volatile("" : "+v"(raw[i]));
 #pragma unroll
     for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(qr[h]));
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 9; ++i) raw[i] = cv ? raw[i] : zero;
 #pragma unroll
     for (int h = 0; h < 2; ++h) qr[h] = rv ? qr[h] : zero;
-    i32x8 oh[2], ol[2];  // this wave's half
+    // the row's largest magnitude: bf16 bit patterns without the sign compare as the
+    // magnitudes do; the 8 lanes l % 8 of a row hold its 512 + 64 elements
+    uint32_t amax = 0;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int i = 0; i < 9; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 r = rv ? raw[kk][c] : zero;
-        float x[8];  // q elements, saturated to the e4m3 range (+-448)
+      for (int e = 0; e < 4; ++e) amax = max(amax, max(raw[i][e] & 0x7fffu, (raw[i][e] >> 16) & 0x7fffu));
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 64));
+    const uint32_t ex = min(max(amax >> 7, 8u), 254u);
+    const float mult = __uint_as_float((261u - ex) << 23);  // 2^(134 - E)
+    // Terms to ring buffer 1, pair region [hi, lo][kb][lane n + 16 j][32 bytes]: this
+    // lane's elements 64 cc + [0, 32) are block kb = cc / 2 of lane group 2 (cc % 2),
+    // the next 32 of lane group 2 (cc % 2) + 1.
+    uint8_t* xo = s_lat[1] + 16384 * rg + 2048 * (cc >> 1) + 32 * ((crow & 15) + 32 * (cc & 1));
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      i32x4 th[2], tl[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 r = raw[4 * hv + i];
+        float x[8];  // scaled q elements: exact, magnitudes below 256
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = fminf(fmaxf(__uint_as_float(r[e] << 16), -448.f), 448.f);
-          x[2 * e + 1] = fminf(fmaxf(__uint_as_float(r[e] & 0xffff0000u), -448.f), 448.f);
+          x[2 * e] = __uint_as_float(r[e] << 16) * mult;
+          x[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u) * mult;
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -315,49 +343,44 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
           w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2], x[4 * h + 3], w, true);
           const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
           const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-          int wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h] - a[0]) * 16.f,
-                                                   (x[4 * h + 1] - a[1]) * 16.f, 0, false);
-          wl = __builtin_amdgcn_cvt_pk_fp8_f32((x[4 * h + 2] - c2[0]) * 16.f,
-                                               (x[4 * h + 3] - c2[1]) * 16.f, wl, true);
-          oh[kk][2 * c + h] = w;
-          ol[kk][2 * c + h] = wl;
+          int wl = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h] - a[0], x[4 * h + 1] - a[1], 0, false);
+          wl = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * h + 2] - c2[0], x[4 * h + 3] - c2[1], wl, true);
+          th[i >> 1][2 * (i & 1) + h] = w;
+          tl[i >> 1][2 * (i & 1) + h] = wl;
         }
       }
-    }
-    // Exchange through ring buffer 1: 16-byte chunk i of lane l at 1024 i + 16 l of
-    // the 8 KB that the partner's copies of tile 1 fill (its keys 16 partner ..
-    // 16 partner + 15).  Each wave reads its own region and waits for the reads
-    // before its first copy of tile 1 overwrites it.
-    auto chunk = [&](const i32x8* v, int i) {
-      const i32x8 x = v[i >> 1];
-      return (i & 1) ? i32x4{x[4], x[5], x[6], x[7]} : i32x4{x[0], x[1], x[2], x[3]};
-    };
-    uint8_t* xo = s_lat[1] + 8192 * partner + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<i32x4*>(xo + 1024 * i) = chunk(oh, i);
-      *reinterpret_cast<i32x4*>(xo + 1024 * (4 + i)) = chunk(ol, i);
+      for (int q2 = 0; q2 < 2; ++q2) {
+        *reinterpret_cast<i32x4*>(xo + 512 * hv + 16 * q2) = th[q2];
+        *reinterpret_cast<i32x4*>(xo + 8192 + 512 * hv + 16 * q2) = tl[q2];
+      }
     }
+    if (cc == 0) s_qex[rg][crow & 15] = ex;
     lds_barrier();
-    const uint8_t* xi = s_lat[1] + 8192 * wave + 16 * lane;
-    i32x4 ph[4], pl[4];
+    const uint8_t* xi = s_lat[1] + 16384 * rg + 32 * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ph[i] = *reinterpret_cast<const i32x4*>(xi + 1024 * i);
-      pl[i] = *reinterpret_cast<const i32x4*>(xi + 1024 * (4 + i));
+    for (int kb = 0; kb < kLat / 128; ++kb) {
+      const u32x4 h0 = *reinterpret_cast<const u32x4*>(xi + 2048 * kb);
+      const u32x4 h1 = *reinterpret_cast<const u32x4*>(xi + 2048 * kb + 16);
+      const u32x4 l0 = *reinterpret_cast<const u32x4*>(xi + 8192 + 2048 * kb);
+      const u32x4 l1 = *reinterpret_cast<const u32x4*>(xi + 8192 + 2048 * kb + 16);
+      qh[kb] = __builtin_bit_cast(i32x8, u32x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]});
+      ql[kb] = __builtin_bit_cast(i32x8, u32x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]});
     }
+    const uint32_t rex = s_qex[rg][n];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const float rmult = __uint_as_float((261u - rex) << 23);
+    c_row = P.c_log2 * __uint_as_float((rex - 7u) << 23);
+    // the rope tail in bf16, scaled by the same power of two (exact)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const i32x8 th = {ph[2 * kk][0], ph[2 * kk][1], ph[2 * kk][2], ph[2 * kk][3],
-                        ph[2 * kk + 1][0], ph[2 * kk + 1][1], ph[2 * kk + 1][2], ph[2 * kk + 1][3]};
-      const i32x8 tl = {pl[2 * kk][0], pl[2 * kk][1], pl[2 * kk][2], pl[2 * kk][3],
-                        pl[2 * kk + 1][0], pl[2 * kk + 1][1], pl[2 * kk + 1][2], pl[2 * kk + 1][3]};
-      qh[kk] = hf ? th : oh[kk];
-      ql[kk] = hf ? tl : ol[kk];
-      qh[2 + kk] = hf ? oh[kk] : th;
-      ql[2 + kk] = hf ? ol[kk] : tl;
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = qr[h][e];
+        const uint32_t lo16 = __float_as_uint(__uint_as_float(w << 16) * rmult) >> 16;
+        const uint32_t hi16 = __float_as_uint(__uint_as_float(w & 0xffff0000u) * rmult) & 0xffff0000u;
+        qr[h][e] = hi16 | lo16;
+      }
   }
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -404,8 +427,7 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
           sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], qh[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-          sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], ql[kb], sacc[tt + e], 0, 0, 0,
-                                                                          kE8M0One, 0, kE8M0Sixteenth);
+          sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], ql[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
         // one copy of the next tile per operand group (8 per tile)
         if (next) copy_pair(k + 1, slot_nx, kb * 2 + tt / 2);
       }
@@ -428,7 +450,7 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
     if (th >= wave_lo && th + 63 <= wave_hi) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        sc[e] = sacc[e >> 2][e & 3] * P.c_log2;
+        sc[e] = sacc[e >> 2][e & 3] * c_row;
         bmax = fmaxf(bmax, sc[e]);
       }
     } else {
@@ -436,7 +458,7 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
       for (int e = 0; e < 16; ++e) {
         const int t = th + 16 * (e >> 2) + 4 * j + (e & 3);
         const bool ok = key_ok(t, row_lo, row_hi, L, tbits, tree);
-        sc[e] = ok ? sacc[e >> 2][e & 3] * P.c_log2 : -INFINITY;
+        sc[e] = ok ? sacc[e >> 2][e & 3] * c_row : -INFINITY;
       }
       if (P.logit_cap > 0.f) {
 #pragma unroll

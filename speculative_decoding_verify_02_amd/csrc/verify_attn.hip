@@ -107,6 +107,9 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
   const int group = a->hq / a->hkv;
   const int rows = group * a->draft_len;
   if (rows > kMaxRows) return VA_EUNSUPPORTED;
+  // the combine's grid has hkv and batch as its y and z dimensions (at most 65535
+  // each): the launchers refuse more, so the gate does too
+  if (a->batch > 65535 || a->hkv > 65535) return VA_EUNSUPPORTED;
 
   if (a->batch > 0) {
     if (check_pointers && (!a->q || !a->k_cache || !a->v_cache || !a->block_table ||
@@ -136,7 +139,12 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
   p->rows = rows;
   const bool fp8 = a->kv_dtype == VA_KV_FP8_E4M3FN;
   int head_groups = a->hkv, per_cu = 1;
-  if (fp8 && a->qk_dim == 576 && rows <= 64) {
+  // the MLA kernel reads V as the first v_dim bytes of the K row it already holds, so
+  // it serves only a V cache that is that view of the K cache; a separate V cache of
+  // the same shape takes the generic kernel
+  const bool v_is_k_view = a->v_cache == a->k_cache && a->v_stride_slot == a->k_stride_slot &&
+                           a->v_stride_head == a->k_stride_head;
+  if (fp8 && a->qk_dim == 576 && rows <= 64 && v_is_k_view) {
     p->kind = kMlaFp8;                      // one workgroup per (head, split), 4 row-group waves
     p->rt = 1;
     p->nrg = 4;

@@ -134,8 +134,11 @@ _CHUNK = 1 << 22
 
 
 def _normal_encoded(seq: np.random.SeedSequence, n: int, kv_dtype: int,
-                    scale: float) -> np.ndarray:
-    """n N(0,1) values, encoded; chunk c of 2^22 values comes from spawn c of ``seq``."""
+                    scale: float, col_mean: Optional[np.ndarray] = None) -> np.ndarray:
+    """n N(0,1) values, encoded; chunk c of 2^22 values comes from spawn c of ``seq``.
+
+    ``col_mean`` (length w) is added to value i as col_mean[i % w]: the values are
+    rows of w columns and column c gets mean col_mean[c]."""
     from concurrent.futures import ThreadPoolExecutor
 
     out = np.empty(n, dtype=np.uint8 if kv_dtype == KV_FP8_E4M3FN else np.uint16)
@@ -145,6 +148,8 @@ def _normal_encoded(seq: np.random.SeedSequence, n: int, kv_dtype: int,
     def draw(c):
         lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
         x = np.random.default_rng(kids[c]).standard_normal(hi - lo)
+        if col_mean is not None:
+            x += col_mean[np.arange(lo, hi) % len(col_mean)]
         if kv_dtype == KV_FP8_E4M3FN:
             out[lo:hi] = _e4m3fn_bytes(x / scale)
         else:
@@ -170,7 +175,7 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
                  num_pages: Optional[int] = None, pool_factor: float = 1.25,
                  seed: int = 0, poison: bool = False, shuffle_pages: bool = True,
                  draft_counts=None, ragged: bool = False, tree: bool = False,
-                 sinks: bool = False, logit_cap: float = 0.0) -> Problem:
+                 sinks: bool = False, logit_cap: float = 0.0, v_mean: float = 0.0) -> Problem:
     """Draw one problem.
 
     ``prefix_lens``: explicit list, or ``prefix_range=(lo, hi)`` for
@@ -188,6 +193,10 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
     slots of extra pages, with a random tree (each draft's parent is an earlier
     draft or the prefix) whose ancestor-or-self relation is ``tree_mask``;
     ``sinks`` draws one N(0, 1) sink logit per q head; ``logit_cap`` is passed on.
+
+    ``v_mean`` gives V column c the mean v_mean * cos(0.37 c + 0.5) (for V aliasing
+    K: the first v_dim columns of the K rows), so outputs are of order v_mean instead
+    of shrinking with the number of keys.
     """
     v_dim = qk_dim if v_dim is None else v_dim
     if sm_scale is None:
@@ -263,16 +272,20 @@ def make_problem(*, name: str = "custom", batch: int, prefix_lens=None,
     q = q.reshape(n_rows, hq, qk_dim)
     owned_pages = np.sort(perm)
 
-    def pool(seq, width):
+    def pool(seq, width, v_cols):
         per_page = page_size * hkv * width
         dt = np.uint8 if kv_dtype == KV_FP8_E4M3FN else np.uint16
         arr = np.zeros((num_pages, per_page), dtype=dt)
+        mean = None
+        if v_mean and v_cols:
+            mean = np.zeros(width)
+            mean[:v_cols] = v_mean * np.cos(0.37 * np.arange(v_cols) + 0.5)
         arr[owned_pages] = _normal_encoded(seq, total_pages * per_page, kv_dtype,
-                                           kv_scale).reshape(total_pages, per_page)
+                                           kv_scale, mean).reshape(total_pages, per_page)
         return arr.reshape(num_slots, hkv, width)
 
-    k = pool(kids[2], qk_dim)
-    v = None if v_aliases_k else pool(kids[3], v_dim)
+    k = pool(kids[2], qk_dim, v_dim if v_aliases_k else 0)
+    v = None if v_aliases_k else pool(kids[3], v_dim, v_dim)
 
     if poison:
         owned = np.zeros(num_slots, dtype=bool)

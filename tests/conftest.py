@@ -25,3 +25,14 @@ def lib():
     """The C-ABI library through its Python binding (fails loudly if it is not built)."""
     from speculative_decoding_verify_02_amd import binding
     return binding.load()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With PARITY_MARGINS_OUT set, write every parity check's worst errors (JSON)."""
+    path = os.environ.get("PARITY_MARGINS_OUT")
+    mod = sys.modules.get("test_verify_attn_gpu")
+    if not path or mod is None or not getattr(mod, "MARGINS", None):
+        return
+    import json
+    with open(path, "w") as f:
+        json.dump(mod.MARGINS, f, indent=0)

@@ -112,11 +112,32 @@ def test_gate_accepts_supported_shapes():
     (dict(hq=64, hkv=1, draft_len=4), B.VA_EUNSUPPORTED),   # 256 rows per KV head
     (dict(k_stride_slot=1 << 31), B.VA_EUNSUPPORTED),       # 4 GiB slot rows (bf16)
     (dict(v_stride_slot=1 << 31), B.VA_EUNSUPPORTED),
+    # the combine's grid takes batch and hkv as dimensions of at most 65535
+    (dict(batch=65536), B.VA_EUNSUPPORTED),
+    (dict(hq=65536, hkv=65536), B.VA_EUNSUPPORTED),
+    (dict(batch=65536, num_splits=1), B.VA_EUNSUPPORTED),
 ])
 def test_gate_rejects(kw, status):
     assert can_handle(**kw) == status
     assert fwd(**kw) == status          # nothing launched: rejected before the launch
     assert combine(**kw) == status
+
+
+def test_largest_grid_dimensions_accepted():
+    assert can_handle(batch=65535) == B.VA_OK
+    assert can_handle(hq=65535, hkv=65535, draft_len=1) == B.VA_OK
+    lib = B.load()
+    assert lib.verify_attn_num_splits(ctypes.byref(fake_args(batch=65536))) == -1
+    assert lib.verify_attn_num_splits(ctypes.byref(fake_args(batch=65535))) >= 1
+
+
+def test_fp8_latent_head_with_separate_v_cache_is_served():
+    # fp8 576/512 with a V cache that is not a view of the K rows is a valid request
+    # (served by the generic kernel, not the one that reads V from the K rows)
+    mla = dict(qk_dim=576, v_dim=512, hq=16, hkv=1, kv_dtype=B.VA_KV_FP8_E4M3FN, k_scale=0.05,
+               v_scale=0.05, k_stride_slot=576, k_stride_head=576)
+    assert can_handle(**mla, v_stride_slot=576, v_stride_head=576) == B.VA_OK
+    assert can_handle(**mla, v_cache=FAKE + 0x100000, v_stride_slot=512, v_stride_head=512) == B.VA_OK
 
 
 def test_workspace_checked_before_launch():

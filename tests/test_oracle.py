@@ -591,3 +591,47 @@ def test_window_pool_translation():
         npg = -(-int(lens0[b]) // 4)
         np.testing.assert_array_equal(bt[b, :npg], pmap[bt0[b, :npg]])
     np.testing.assert_array_equal(lens, lens0)
+
+
+# ---------------------------------------------------------------------------
+# the checker behind every GPU parity assertion
+# ---------------------------------------------------------------------------
+
+def test_allclose_report_bounds_and_failures():
+    """|got - ref| <= atol + rtol |ref| elementwise: a pair just inside passes, a pair just
+    outside fails (by atol alone at ref = 0 and by rtol at large |ref|), NaN or inf in
+    the result fails, NaN in the reference is skipped."""
+    tol = 1e-2
+    ref = np.array([0.0, 1.0, -2.0, 50.0, 1e-6])
+    bound = tol + tol * np.abs(ref)
+    ok, err, excess = oracle.allclose_report(ref, ref, tol, tol)
+    assert ok and err == 0.0 and excess < 0
+    ok, _, _ = oracle.allclose_report(ref + 0.999 * bound, ref, tol, tol)
+    assert ok
+    ok, _, _ = oracle.allclose_report(ref - 0.999 * bound, ref, tol, tol)
+    assert ok
+    for i in range(len(ref)):
+        for sign in (1.0, -1.0):
+            got = ref.copy()
+            got[i] += sign * 1.001 * bound[i]
+            ok, err, excess = oracle.allclose_report(got, ref, tol, tol)
+            assert not ok and excess > 0, (i, sign)
+            assert math.isclose(err, 1.001 * bound[i], rel_tol=1e-9)
+    # rtol is relative to the reference, not to the result
+    ok, _, _ = oracle.allclose_report(np.array([100.0 + 1.0 + 0.011]), np.array([100.0]), tol, tol)
+    assert not ok
+    for bad in (math.nan, math.inf, -math.inf):
+        got = ref.copy()
+        got[2] = bad
+        ok, err, excess = oracle.allclose_report(got, ref, tol, tol)
+        assert not ok and err == math.inf and excess == math.inf
+    # a NaN in the reference marks an element that was not computed: skipped
+    r2 = ref.copy()
+    r2[1] = math.nan
+    got = ref.copy()
+    got[1] = 123.0
+    assert oracle.allclose_report(got, r2, tol, tol)[0]
+    assert oracle.allclose_report(np.zeros(3), np.full(3, math.nan), tol, tol)[0]
+    # shapes must agree element for element (a transposed result is not accepted)
+    a = np.arange(6.0).reshape(2, 3)
+    assert not oracle.allclose_report(a.T.reshape(2, 3), a, tol, tol)[0]
