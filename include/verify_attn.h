@@ -247,6 +247,27 @@ int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int3
 int verify_attn_translate_slots(const int32_t* in, int64_t n, const int32_t* full_to_swa,
                                 int64_t map_len, int32_t* out, void* stream);
 
+/*
+ * verify_attn_fwd followed by verify_attn_combine, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the partials live in a static per-device array of
+ * VERIFY_ATTN_STATIC_SCRATCH_BYTES bytes (64 MiB) that the library's code object
+ * holds on each device it runs on until the process ends, instead of in the caller's
+ * workspace.  args->workspace and args->workspace_bytes are ignored.  The call makes
+ * no allocation (no hipMalloc, no allocating library routine).
+ *   num_splits = 0: the heuristic's slot count, lowered to the most the array holds;
+ *   num_splits > 0: that count, or VA_EWORKSPACE when its partials
+ *   (verify_attn_workspace_bytes) exceed the array.  VA_EWORKSPACE also when not even
+ *   one slot per sequence fits.  Other errors as for verify_attn_fwd; VA_EHIP if the
+ *   array's device address cannot be obtained.
+ * Nothing in the array needs clearing between calls (the combine reads only what the
+ * split-KV pass of the same call wrote), but every call on one device shares that
+ * device's array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.
+ */
+#define VERIFY_ATTN_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+int verify_attn_fwd_combine_noalloc(const verify_attn_args* args, void* stream);
+
 /* Text for a status code (static storage). */
 const char* verify_attn_strerror(int status);
 

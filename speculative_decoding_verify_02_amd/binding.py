@@ -32,7 +32,11 @@ EXPORTED = (
     "verify_attn_strerror",
     "verify_attn_abi_version",
     "verify_attn_translate_slots",
+    "verify_attn_fwd_combine_noalloc",
 )
+
+# bytes of the static per-device array verify_attn_fwd_combine_noalloc uses
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class VerifyAttnArgs(ctypes.Structure):
@@ -131,7 +135,7 @@ def load(path: Optional[str] = None):
     args_p = ctypes.POINTER(VerifyAttnArgs)
     lib.verify_attn_build_block_table.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.verify_attn_build_block_table.restype = ctypes.c_int
-    for name in ("verify_attn_fwd", "verify_attn_combine"):
+    for name in ("verify_attn_fwd", "verify_attn_combine", "verify_attn_fwd_combine_noalloc"):
         getattr(lib, name).argtypes = [args_p, vp]
         getattr(lib, name).restype = ctypes.c_int
     lib.verify_attn_can_handle.argtypes = [args_p]
@@ -401,6 +405,17 @@ def verify_attn_combine(call: VerifyCall, stream=None, check=True) -> int:
     st = load().verify_attn_combine(ctypes.byref(call.args), _stream_ptr(stream))
     if check:
         _check("verify_attn_combine", st)
+    return st
+
+
+def verify_attn_fwd_combine_noalloc(call: VerifyCall, stream=None, check=True) -> int:
+    """fwd + combine with the library's static per-device scratch instead of the call's
+    workspace (for callers that cannot allocate); calls overlapping on one GPU race."""
+    if _debug_validate:
+        validate_call(call)
+    st = load().verify_attn_fwd_combine_noalloc(ctypes.byref(call.args), _stream_ptr(stream))
+    if check:
+        _check("verify_attn_fwd_combine_noalloc", st)
     return st
 
 

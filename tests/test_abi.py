@@ -140,6 +140,25 @@ def test_fp8_latent_head_with_separate_v_cache_is_served():
     assert can_handle(**mla, v_cache=FAKE + 0x100000, v_stride_slot=512, v_stride_head=512) == B.VA_OK
 
 
+def noalloc(**kw):
+    return B.load().verify_attn_fwd_combine_noalloc(ctypes.byref(fake_args(**kw)), None)
+
+
+def test_noalloc_rejects_before_any_launch():
+    # the same argument checks as fwd; the caller's workspace fields are ignored
+    assert noalloc(q=None) == B.VA_EINVAL
+    assert noalloc(draft_len=9) == B.VA_EUNSUPPORTED
+    assert noalloc(batch=0, workspace=None, workspace_bytes=0) == B.VA_OK
+    # partials beyond the static array: an explicit slot count that does not fit, and a
+    # batch for which not even one slot per sequence fits (2000 x 2 x 16 rows x 513 x 4 B)
+    per_slot = B.verify_attn_workspace_bytes(2, 2, 8, 4, 128, 1) - 2 * 4
+    fit = (B.STATIC_SCRATCH_BYTES - 8) // per_slot
+    assert noalloc(num_splits=fit + 1) == B.VA_EWORKSPACE
+    assert noalloc(batch=2000, qk_dim=576, v_dim=512, hq=16, hkv=1, kv_dtype=B.VA_KV_FP8_E4M3FN,
+                   k_scale=0.05, v_scale=0.05, k_stride_slot=576, k_stride_head=576,
+                   v_stride_slot=576, v_stride_head=576, num_splits=0) == B.VA_EWORKSPACE
+
+
 def test_workspace_checked_before_launch():
     need = B.verify_attn_workspace_bytes(2, 2, 8, 4, 128, 4)
     assert need == (2 * 2 * 4 * 16 * 129 + 2) * 4     # partials + one piece count per sequence
