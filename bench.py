@@ -1,26 +1,33 @@
 """Benchmark: EAGLE target-verify attention (topk = 1) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--all-configs]
+                    [--extensions] [--p3-sweep]
 
 One step = the whole path on one batch: block-table scatter, split-KV pass over
 the prefix and the causal draft keys, log-sum-exp combine.  Inputs are seeded synthetic workloads
 resident in HBM before timing starts.  Prints ONE JSON line:
 
-  value          KV-read GB/s of the whole step (algorithmic bytes / step time;
-                 K steps between two synchronisations, nothing else on the stream)
+  value          KV-read GB/s of the whole step on the headline workload (the
+                 long-context batch): algorithmic bytes / step time, K steps between
+                 two synchronisations, nothing else on the stream
   us_per_call    verify_attn_fwd + verify_attn_combine, K calls back to back
                  between two HIP events; call_pct_of_peak is its KV-read share of
                  the 8 TB/s HBM peak
+  call_us        per call (events around fwd + combine only): median, p10, p90;
+                 call_us_flushed the same with a 1 GiB read before each call
   roofline       the split-KV kernel (the dominant one): algorithmic bytes per
-                 launch / its mean launch time from HIP events on its stream,
-                 against the 8 TB/s HBM peak
+                 launch / its mean launch time (K launches back to back between two
+                 HIP events on its stream), against the 8 TB/s HBM peak
   event_gap_us   what one recorded event adds to an interval on this stream
   cpu_baseline   the fp64 oracle timed on a bounded sample of the same workload
-  per_config     (with --all-configs) the other large workloads, same protocol
+  per_config     the other two target workloads (sliding-window GQA, MLA share),
+                 same protocol and their own roofline; with --all-configs also the
+                 two small ones
+  p3_sweep       (--p3-sweep) the split-KV page's kernel shape across contexts
 
-Workloads whose read set fits the 256 MB Infinity Cache are run over several
-copies of the KV pool in rotation so every step reads memory the previous steps
-did not touch.
+Workloads whose read set is not at least twice the 256 MB Infinity Cache run over
+several copies of the KV pool in rotation, so every step reads memory at least
+512 MB of other reads have passed since.
 """
 
 from __future__ import annotations
@@ -102,25 +109,46 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int, workload: str,
     return out
 
 
-def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides=None,
-            label=None):
+def kv_copies_for(kv_bytes: int) -> int:
+    """KV pool copies to rotate through: enough that at least 2x the Infinity Cache of
+    other reads passes between two reads of one copy (1 when the read set is that big)."""
+    if kv_bytes >= 2 * CACHE_BYTES:
+        return 1
+    return min(64, 1 + -(-2 * CACHE_BYTES // max(kv_bytes, 1)))
+
+
+def kernel_name(p) -> str:
+    """The split-KV kernel the library picks for a workload (the dominant one)."""
+    from speculative_decoding_verify_02_amd import workloads as W
+    if p.kv_dtype == W.KV_FP8_E4M3FN and p.qk_dim == 576 and p.v_aliases_k and \
+            (p.hq // p.hkv) * p.draft_len <= 64:
+        return "splitkv_mla_fp8_kernel"
+    if p.kv_dtype == W.KV_BF16 and p.qk_dim == 256 and (p.hq // p.hkv) * p.draft_len <= 64:
+        return "splitkv_tile_kernel"
+    return "splitkv_fwd_kernel"
+
+
+def _dist(xs):
+    xs = sorted(xs)
+    pick = lambda f: xs[min(len(xs) - 1, int(f * (len(xs) - 1) + 0.5))]
+    return {"median": round(pick(0.5), 2), "p10": round(pick(0.1), 2), "p90": round(pick(0.9), 2)}
+
+
+def measure(p, steps: int, warmup: int, splits=None, log=print, flushed=True):
+    """Time one workload (a workloads.Problem) with the passes the JSON line reports."""
     import torch
 
     from speculative_decoding_verify_02_amd import binding
     from speculative_decoding_verify_02_amd import workloads as W
     from speculative_decoding_verify_02_amd.runner import DeviceProblem
 
-    t0 = time.time()
-    p = W.make_config(idx, **(overrides or {}))
-    if label:
-        p.name = label
-    log(f"[bench] config {idx} {p.name}: inputs drawn in {time.time() - t0:.1f}s")
     kv_bytes = W.algorithmic_kv_bytes(p)
     fwd_bytes = kv_bytes  # the split-KV pass reads every visible key, draft keys included
-    copies = 1 if kv_bytes > 2 * CACHE_BYTES else 3
+    copies = kv_copies_for(kv_bytes)
     dp = DeviceProblem(p, device="cuda", num_splits=splits, kv_copies=copies)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    new_event = lambda: torch.cuda.Event(enable_timing=True)
 
     for w in range(warmup):
         dp.step(copy=w % copies)
@@ -138,7 +166,7 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides
 
     # pass 2: the verify call (verify_attn_fwd + verify_attn_combine) K times back to
     # back between two events
-    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea, eb = new_event(), new_event()
     torch.cuda.synchronize()
     ea.record(stream)
     for k in range(steps):
@@ -148,9 +176,50 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides
     torch.cuda.synchronize()
     call_b2b_us = ea.elapsed_time(eb) * 1e3 / steps
 
-    # pass 3: events around each kernel of each step, for the per-kernel split (each
+    # pass 3: the split-KV kernel alone, K launches back to back between two events on
+    # its stream: its mean launch time for the roofline (no event inside the interval)
+    ea, eb = new_event(), new_event()
+    torch.cuda.synchronize()
+    ea.record(stream)
+    for k in range(steps):
+        binding.verify_attn_fwd(dp.calls[k % copies])
+    eb.record(stream)
+    torch.cuda.synchronize()
+    fwd_b2b_us = ea.elapsed_time(eb) * 1e3 / steps
+
+    # pass 4: events around each call (fwd + combine, no event between them): the
+    # per-call distribution
+    ev = [(new_event(), new_event()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        binding.verify_attn_fwd(dp.calls[k % copies])
+        binding.verify_attn_combine(dp.calls[k % copies])
+        e1.record(stream)
+    torch.cuda.synchronize()
+    call_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+
+    # pass 5: the same with a 1 GiB read before each call, outside the timed interval,
+    # so no byte of the call's read set is left in the L2s or the Infinity Cache (a read,
+    # not a fill: a fill leaves dirty lines whose write-back would land in the call)
+    call_flushed = None
+    if flushed:
+        flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+        ev = [(new_event(), new_event()) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k, (e0, e1) in enumerate(ev):
+            flush.sum()
+            e0.record(stream)
+            binding.verify_attn_fwd(dp.calls[k % copies])
+            binding.verify_attn_combine(dp.calls[k % copies])
+            e1.record(stream)
+        torch.cuda.synchronize()
+        call_flushed = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+        del flush
+
+    # pass 6: events around each kernel of each step, for the per-kernel split (each
     # interval includes one event's own cost, measured below as an empty interval)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[new_event() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for k in range(steps):
         c = k % copies
@@ -165,7 +234,7 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides
     torch.cuda.synchronize()
     gaps = []
     for _ in range(20):
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0, g1 = new_event(), new_event()
         g0.record(stream)
         g1.record(stream)
         torch.cuda.synchronize()
@@ -175,31 +244,68 @@ def measure(idx: int, steps: int, warmup: int, splits=None, log=print, overrides
     bt_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     comb_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
-    # fwd + combine per step, the verify-attention call time
-    call_us = sorted(e[1].elapsed_time(e[3]) * 1e3 for e in ev)   # with the event between
-    pct = lambda f: call_us[min(len(call_us) - 1, int(f * (len(call_us) - 1) + 0.5))]
     ms_per_step = wall * 1e3 / steps
     rec = dict(
-        idx=idx, name=p.name, p=p, kv_bytes=kv_bytes, fwd_bytes=fwd_bytes,
+        name=p.name, p=p, kv_bytes=kv_bytes, fwd_bytes=fwd_bytes, kernel=kernel_name(p),
         ms_per_step=ms_per_step, bt_us=bt_ms * 1e3, fwd_us=fwd_ms * 1e3, comb_us=comb_ms * 1e3,
-        splits=dp.splits, copies=copies, call_b2b_us=call_b2b_us, event_gap_us=event_gap_us,
-        call_us={"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2)},
+        fwd_b2b_us=fwd_b2b_us, splits=dp.splits, copies=copies, call_b2b_us=call_b2b_us,
+        event_gap_us=event_gap_us, call_us=_dist(call_us),
+        call_us_flushed=None if call_flushed is None else _dist(call_flushed),
         step_gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
-        fwd_gbs=fwd_bytes / (fwd_ms * 1e-3) / 1e9,
-        kernels_gbs=kv_bytes / ((bt_ms + fwd_ms + comb_ms) * 1e-3) / 1e9,
+        fwd_gbs=fwd_bytes / (fwd_b2b_us * 1e-6) / 1e9,
         flops=W.algorithmic_flops(p),
-        mfma_dtype="fp8" if (p.kv_dtype == W.KV_FP8_E4M3FN and p.qk_dim == 576) else "bf16",
+        mfma_dtype="fp8" if kernel_name(p) == "splitkv_mla_fp8_kernel" else "bf16",
     )
-    rec["mfma_tflops"] = rec["flops"] / (fwd_ms * 1e-3) / 1e12
-    log(f"[bench] config {idx}: {ms_per_step * 1e3:.1f} us/step (bt {rec['bt_us']:.1f} + fwd "
+    rec["mfma_tflops"] = rec["flops"] / (fwd_b2b_us * 1e-6) / 1e12
+    log(f"[bench] {p.name}: {ms_per_step * 1e3:.1f} us/step (events: bt {rec['bt_us']:.1f} + fwd "
         f"{rec['fwd_us']:.1f} + combine {rec['comb_us']:.1f} us), KV {kv_bytes / 1e6:.1f} MB, "
-        f"step {rec['step_gbs']:.0f} GB/s, fwd {rec['fwd_gbs']:.0f} GB/s "
-        f"({100 * rec['fwd_gbs'] / HBM_PEAK_GBS:.1f}% of peak), call back to back {call_b2b_us:.1f} us "
-        f"({100 * kv_bytes / (call_b2b_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.1f}% of peak), "
-        f"event gap {event_gap_us:.1f} us, splits {dp.splits}")
+        f"step {rec['step_gbs']:.0f} GB/s, fwd back to back {fwd_b2b_us:.1f} us "
+        f"({100 * rec['fwd_gbs'] / HBM_PEAK_GBS:.1f}% of peak), call back to back "
+        f"{call_b2b_us:.1f} us ({100 * kv_bytes / (call_b2b_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.1f}% "
+        f"of peak), call median {rec['call_us']['median']} us"
+        + (f", flushed {rec['call_us_flushed']['median']} us" if call_flushed else "")
+        + f", event gap {event_gap_us:.1f} us, splits {dp.splits}, KV copies {copies}")
     del dp
     torch.cuda.empty_cache()
     return rec
+
+
+def measure_config(idx: int, steps: int, warmup: int, splits=None, log=print, overrides=None,
+                   label=None, flushed=True):
+    from speculative_decoding_verify_02_amd import workloads as W
+    t0 = time.time()
+    p = W.make_config(idx, **(overrides or {}))
+    if label:
+        p.name = label
+    log(f"[bench] config {idx} {p.name}: inputs drawn in {time.time() - t0:.1f}s")
+    r = measure(p, steps, warmup, splits, log, flushed)
+    r["idx"] = idx
+    return r
+
+
+def p3_sweep(steps: int, warmup: int, log=print):
+    """The split-KV page's kernel shape (H_Q 16, H_KV 2, head_dim 256, 4 draft tokens,
+    bf16, batch 1) across contexts, and the 16k point at batch 16: the page's ~536 MB
+    of K + V read in 0.79 ms on MI350X by the prefill-kernel fallback ("Motivation").
+    The page's table does not give a page size; the Triton backend's token-level pool
+    (page size 1, shuffled slots) is used here."""
+    from speculative_decoding_verify_02_amd import workloads as W
+    out = {}
+    for batch, ctx in [(1, 2048), (1, 4096), (1, 8192), (1, 16384), (1, 32768), (16, 16384)]:
+        name = f"p3-b{batch}-ctx{ctx}"
+        p = W.make_problem(name=name, batch=batch, prefix_lens=[ctx] * batch, draft_len=4, hq=16,
+                           hkv=2, qk_dim=256, v_dim=256, page_size=1, seed=1100 + ctx + batch)
+        r = measure(p, steps, warmup, None, log, flushed=False)
+        out[name] = {"call_us_back_to_back": round(r["call_b2b_us"], 2),
+                     "call_us": r["call_us"], "kv_mb": round(r["kv_bytes"] / 1e6, 2),
+                     "call_gbs": round(r["kv_bytes"] / (r["call_b2b_us"] * 1e-6) / 1e9, 1),
+                     "call_pct_of_peak": round(100 * r["kv_bytes"] / (r["call_b2b_us"] * 1e-6)
+                                               / 1e9 / HBM_PEAK_GBS, 2),
+                     "splits": r["splits"], "kv_copies": r["copies"]}
+        if batch == 16:
+            out[name]["page_figure"] = ("split-KV page, Motivation: ~536 MB of K+V in 0.79 ms "
+                                        "(~680 GB/s) on MI350X with the prefill fallback")
+    return out
 
 
 def time_translation(steps: int, log=print):
@@ -244,17 +350,18 @@ def time_translation(steps: int, log=print):
 
 
 def cpu_baseline(p, budget_s: float = 12.0, log=print):
-    """The oracle as it stands on a bounded prefix of the workload's sequences, BLAS
-    pinned to one thread (so `cores` is exactly what ran)."""
+    """The oracle as it stands on a bounded prefix of the workload's sequences, with as
+    many BLAS threads as this process may run on (the count is reported as `cores`)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     from speculative_decoding_verify_02_amd import workloads as W
 
+    cores = len(os.sched_getaffinity(0))
     per_tok = p.hkv * (p.qk_dim + (0 if p.v_aliases_k else p.v_dim)) * p.elem_bytes
     done_bytes, nseq = 0, 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         for b in range(p.batch):
             rows = list(range(b * p.draft_len, (b + 1) * p.draft_len))
             oracle.run(p, rows=rows)
@@ -264,10 +371,12 @@ def cpu_baseline(p, budget_s: float = 12.0, log=print):
             if time.perf_counter() - t0 > budget_s:
                 break
     dt = time.perf_counter() - t0
-    log(f"[bench] cpu oracle: {nseq} of {p.batch} sequences in {dt:.1f}s")
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    log(f"[bench] cpu oracle: {nseq} of {p.batch} sequences in {dt:.1f}s, {cores} BLAS threads")
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
             "sample": f"{nseq} of {p.batch} sequences of {p.name} (all draft rows and heads), "
-                      f"{done_bytes / 1e6:.1f} MB of KV in {dt:.1f}s, fp64 NumPy, BLAS 1 thread"}
+                      f"{done_bytes / 1e6:.1f} MB of KV in {dt:.1f}s, fp64 NumPy, BLAS threads = "
+                      f"{cores} (len(os.sched_getaffinity(0)))"}
 
 
 def workload_config(p) -> dict:
@@ -285,12 +394,18 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="headline workload index")
-    ap.add_argument("--all-configs", action="store_true", help="also time the other large workloads")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload alone (no per_config entries)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time the two small workloads (launch-bound)")
     ap.add_argument("--extensions", action="store_true",
                     help="also time draft-extend rows, tree verify, sinks + logit cap and the "
                          "window-pool slot translation")
+    ap.add_argument("--p3-sweep", action="store_true",
+                    help="also time the split-KV page's kernel shape across contexts")
     ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="skip the flushed-cache pass")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, issue one plain device copy of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -300,8 +415,10 @@ def main():
     if args.traffic_from:
         from speculative_decoding_verify_02_amd import workloads as W
         name = W.CONFIG_NAMES[args.config]
+        p = W.make_config(args.config)
         rec = traffic_from(args.traffic_from[0], args.traffic_from[1],
-                           args.copy_calibration_mib or 1024, name)
+                           args.copy_calibration_mib or 1024, name, kernel_key=kernel_name(p))
+        rec["algorithmic_kv_bytes"] = W.algorithmic_kv_bytes(p)
         path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
@@ -325,37 +442,53 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    src_hash = kernel_source_hash()
+
     def mfma_summary(r):
-        # algorithmic matrix flops of the split-KV pass over its event time, against the
-        # dense peak of the MFMA type the kernel runs
+        # algorithmic matrix flops of the split-KV pass over its mean launch time, against
+        # the dense peak of the MFMA type the kernel runs
         peak = MFMA_PEAK_TFLOPS[r["mfma_dtype"]]
         return {"dtype": r["mfma_dtype"], "algorithmic_flops_per_launch": r["flops"],
                 "achieved_tflops": round(r["mfma_tflops"], 1), "peak_tflops": peak,
                 "frac": round(r["mfma_tflops"] / peak, 4)}
 
+    def roofline(r):
+        return {"bound": "hbm", "achieved": round(r["fwd_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(r["fwd_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(r["name"], src_hash), "kernel": r["kernel"],
+                "algorithmic_bytes_per_launch": r["fwd_bytes"],
+                "mean_launch_us": round(r["fwd_b2b_us"], 2)}
+
+    def call_pct(r):
+        return round(100 * r["kv_bytes"] / (r["call_b2b_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
+
     def summary(r):
         return {
-            "us_per_step": round(r["ms_per_step"] * 1e3, 2), "fwd_us": round(r["fwd_us"], 2),
-            "combine_us": round(r["comb_us"], 2), "block_table_us": round(r["bt_us"], 2),
+            "config": workload_config(r["p"]),
             "kv_mb": round(r["kv_bytes"] / 1e6, 2),
-            "step_gbs": round(r["step_gbs"], 1), "fwd_gbs": round(r["fwd_gbs"], 1),
-            "fwd_pct_of_peak": round(100 * r["fwd_gbs"] / HBM_PEAK_GBS, 2),
-            "kernels_pct_of_peak": round(100 * r["kernels_gbs"] / HBM_PEAK_GBS, 2),
+            "us_per_step": round(r["ms_per_step"] * 1e3, 2),
             "call_us_back_to_back": round(r["call_b2b_us"], 2),
-            "call_pct_of_peak": round(100 * r["kv_bytes"] / (r["call_b2b_us"] * 1e-6)
-                                      / 1e9 / HBM_PEAK_GBS, 2),
-            "call_us_with_event_between": r["call_us"],
+            "call_pct_of_peak": call_pct(r),
+            "call_us": r["call_us"],
+            "call_us_flushed": r["call_us_flushed"],
+            "kernel_us_with_events": {"block_table": round(r["bt_us"], 2),
+                                      "splitkv_fwd": round(r["fwd_us"], 2),
+                                      "combine": round(r["comb_us"], 2)},
+            "roofline": roofline(r),
             "mfma": mfma_summary(r),
             "splits": r["splits"], "kv_copies": r["copies"]}
 
-    head = measure(args.config, args.steps, args.warmup, args.splits, log)
+    flushed = not args.no_flush
+    head = measure_config(args.config, args.steps, args.warmup, args.splits, log, flushed=flushed)
     per_config = {}
+    others = [] if args.only else [3, 4]
     if args.all_configs:
-        for idx in (0, 1, 2, 3, 4):
-            if idx == args.config:
-                continue
-            r = measure(idx, args.steps, args.warmup, None, log)
-            per_config[r["name"]] = summary(r)
+        others = [0, 1, 2, 3, 4]
+    for idx in others:
+        if idx == args.config:
+            continue
+        r = measure_config(idx, args.steps, args.warmup, None, log, flushed=flushed)
+        per_config[r["name"]] = summary(r)
     extensions = {}
     if args.extensions:
         # the version 2 extensions on the long-context batch (and the MLA share)
@@ -364,9 +497,11 @@ def main():
                 (2, dict(tree=True), "long-context-batch+tree-verify"),
                 (2, dict(sinks=True, logit_cap=30.0), "long-context-batch+sinks+logit-cap"),
                 (4, dict(tree=True), "mla-fp8-share+tree-verify")):
-            r = measure(idx, args.steps, args.warmup, None, log, overrides=over, label=label)
+            r = measure_config(idx, args.steps, args.warmup, None, log, overrides=over,
+                               label=label, flushed=False)
             extensions[label] = summary(r)
         extensions["window-pool-slot-translation"] = time_translation(args.steps, log)
+    p3 = p3_sweep(args.steps, args.warmup, log) if args.p3_sweep else None
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 19     # bf16 elements
@@ -378,14 +513,7 @@ def main():
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB issued")
         del src, dst
 
-    src_hash = kernel_source_hash()
     p = head["p"]
-    traffic = traffic_for(p.name, src_hash)
-    roof = {"bound": "hbm", "achieved": round(head["fwd_gbs"], 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(head["fwd_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "kernel": "splitkv_fwd_kernel",
-            "algorithmic_bytes_per_launch": head["fwd_bytes"],
-            "mean_launch_us": round(head["fwd_us"], 2)}
     cpu = None if args.no_cpu_baseline else cpu_baseline(p, log=log)
 
     out = {
@@ -407,15 +535,17 @@ def main():
         "config": dict(workload_config(p), splits=head["splits"], kv_copies=head["copies"],
                        kv_mb=round(head["kv_bytes"] / 1e6, 2)),
         # the call's share of peak: algorithmic KV bytes over the back-to-back call time
-        "call_pct_of_peak": round(100 * head["kv_bytes"] / (head["call_b2b_us"] * 1e-6)
-                                  / 1e9 / HBM_PEAK_GBS, 2),
-        # per call with an event between the two kernels (median, p10, p90)
-        "call_us_with_event_between": head["call_us"],
+        "call_pct_of_peak": call_pct(head),
+        # per call, events around fwd + combine only (median, p10, p90), and the same
+        # with a 1 GiB read before each call (nothing of the read set left in any cache)
+        "call_us": head["call_us"],
+        "call_us_flushed": head["call_us_flushed"],
         # per kernel, events around each launch (each includes one event's own cost)
-        "kernel_us": {"block_table": round(head["bt_us"], 2), "splitkv_fwd": round(head["fwd_us"], 2),
-                      "combine": round(head["comb_us"], 2)},
+        "kernel_us_with_events": {"block_table": round(head["bt_us"], 2),
+                                  "splitkv_fwd": round(head["fwd_us"], 2),
+                                  "combine": round(head["comb_us"], 2)},
         "event_gap_us": round(head["event_gap_us"], 2),
-        "roofline": roof,
+        "roofline": roofline(head),
         # the same kernel against the matrix cores (an HBM-bound kernel sits far below)
         "mfma": mfma_summary(head),
         "cpu_baseline": cpu,
@@ -424,6 +554,8 @@ def main():
         out["per_config"] = per_config
     if extensions:
         out["extensions"] = extensions
+    if p3:
+        out["p3_sweep"] = p3
     print(json.dumps(out), flush=True)
 
 
