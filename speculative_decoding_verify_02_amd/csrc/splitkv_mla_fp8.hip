@@ -407,38 +407,58 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
     f32x4 sacc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // d < 512: fp8 x fp8 (K bytes as they are, q as hi + lo terms).  Token tiles go
-    // in pairs so the two products into one accumulator are not back to back.
+    // d < 512: fp8 x fp8 (K bytes as they are, q as hi + lo terms), in 8 operand groups
+    // g = (kb, token-tile pair): the two 16-key operands of group g + 1 are read from
+    // LDS before the four products of group g issue, so their latency runs under the
+    // matrix instructions.  Token tiles go in pairs so the two products into one
+    // accumulator are not back to back.
+    auto k_operands = [&](int g, i32x8* ka) {
+      const int kb = g >> 1, tt = 2 * (g & 1);
 #pragma unroll
-    for (int kb = 0; kb < kLat / 128; ++kb) {
-#pragma unroll
-      for (int tt = 0; tt < 4; tt += 2) {
-        i32x8 ka[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int x = (kb ^ (tt + e)) & 1;
-          const int imm = 8192 * (tt + e) + 256 * (kb >> 1);
-          const u32x4 k0 = *reinterpret_cast<const u32x4*>(lat + qoff[0][x] + imm);
-          const u32x4 k1 = *reinterpret_cast<const u32x4*>(lat + qoff[1][x] + imm);
-          ka[e] = __builtin_bit_cast(i32x8, u32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], qh[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[e], ql[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
-        // one copy of the next tile per operand group (8 per tile)
-        if (next) copy_pair(k + 1, slot_nx, kb * 2 + tt / 2);
+      for (int e = 0; e < 2; ++e) {
+        const int x = (kb ^ (tt + e)) & 1;
+        const int imm = 8192 * (tt + e) + 256 * (kb >> 1);
+        const u32x4 k0 = *reinterpret_cast<const u32x4*>(lat + qoff[0][x] + imm);
+        const u32x4 k1 = *reinterpret_cast<const u32x4*>(lat + qoff[1][x] + imm);
+        ka[e] = __builtin_bit_cast(i32x8, u32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
       }
+    };
+    // rope operands (bf16 k-steps, lane group j holds 512 + 32h + 8j + [0, 8)), read
+    // with the last latent group
+    u32x2 kr[2][4];
+    i32x8 kc[2], kn[2];
+    k_operands(0, kc);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int kb = g >> 1, tt = 2 * (g & 1);
+      if (g < 7) {
+        k_operands(g + 1, kn);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4)
+            kr[h][t4] = *reinterpret_cast<const u32x2*>(s_rope + roff[h] + 16 * kRope * t4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc[e], qh[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        sacc[tt + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc[e], ql[kb], sacc[tt + e], 0, 0, 0, 0, 0, 0);
+      // one copy of the next tile per operand group (8 per tile)
+      if (next) copy_pair(k + 1, slot_nx, g);
+      __builtin_amdgcn_sched_barrier(0);
+      kc[0] = kn[0];
+      kc[1] = kn[1];
     }
-    // rope tail d in [512, 576): bf16 k-steps, lane group j holds 512 + 32h + 8j + [0, 8)
+    // rope tail d in [512, 576): bf16 products with K widened exactly
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const u32x2 kr = *reinterpret_cast<const u32x2*>(s_rope + roff[h] + 16 * kRope * tt);
-        const u32x2 w0 = fp8x4_to_bf16x4(kr[0]), w1 = fp8x4_to_bf16x4(kr[1]);
+        const u32x2 w0 = fp8x4_to_bf16x4(kr[h][tt][0]), w1 = fp8x4_to_bf16x4(kr[h][tt][1]);
         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(u32x4{w0[0], w0[1], w1[0], w1[1]}), as_bf16x8(qr[h]), sacc[tt], 0, 0, 0);
       }
@@ -521,11 +541,11 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
     l_run = l_run * alpha + psum;
     m_run = m_new;
 
-    // a5: O^T += V^T P^T over all 128 keys, this wave's 256 columns
+    // a5: O^T += V^T P^T over all 128 keys, this wave's 256 columns, two column tiles
+    // per step: the V^T operands of step s + 1 are read from LDS before the four
+    // products of step s issue
     __attribute__((address_space(3))) char* lbase = (__attribute__((address_space(3))) char*)lat;
-#pragma unroll
-    for (int ct = 0; ct < kCT; ct += 2) {
-      i32x8 a[2];
+    auto v_operands = [&](int ct, i32x8* a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
 #pragma unroll
@@ -536,13 +556,23 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
           a[e][2 * r + 1] = x[1];
         }
       }
+    };
+    i32x8 vc[2], vn[2];
+    v_operands(0, vc);
+#pragma unroll
+    for (int ct = 0; ct < kCT; ct += 2) {
+      if (ct + 2 < kCT) v_operands(ct + 2, vn);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pb, oacc[ct + e], 0, 0, 0, 0, 0, 0);
+        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vc[e], pb, oacc[ct + e], 0, 0, 0, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[e], pb_lo, oacc[ct + e], 0, 0, 0,
+        oacc[ct + e] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vc[e], pb_lo, oacc[ct + e], 0, 0, 0,
                                                                         kE8M0One, 0, kE8M0Sixteenth);
+      __builtin_amdgcn_sched_barrier(0);
+      vc[0] = vn[0];
+      vc[1] = vn[1];
     }
   }
 
