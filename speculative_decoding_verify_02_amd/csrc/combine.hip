@@ -167,6 +167,95 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   if (P.lse && lane == 0) P.lse[(int64_t)r * (P.hkv * P.group) + h] = M + logf(Z);
 }
 
+// Rows whose sequence may span many pieces (the slot count is large when few
+// sequences spread over the whole chip): W waves share one row, wave w merging pieces
+// w, w + W, w + 2W, ... against its own maximum, so W times as many partial rows are
+// in flight; wave 0 then merges the W results through LDS.  One row per workgroup,
+// so every wave takes the same exits and all of them reach the one barrier.
+template <int DV, int W>
+__global__ __launch_bounds__(64 * W) void combine_split_kernel(CombineParams P) {
+  constexpr int CPT = DV / 64;  // output columns per lane
+  constexpr int NB = 8;         // partial rows in flight per wave
+  __shared__ float s_acc[W][DV];
+  __shared__ float s_mz[W][2];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int row = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  if (row >= P.rows) return;
+  const int i = row / P.group;
+  const int nrow_b = P.qo_indptr ? P.qo_indptr[b + 1] - P.qo_indptr[b] : P.draft;
+  if (i >= nrow_b) return;
+  const int h = g * P.group + row % P.group;
+  const int r = (P.qo_indptr ? P.qo_indptr[b] : b * P.draft) + i;
+
+  int n = P.counts[b];
+  n = n < 1 ? 1 : (n > P.slots ? P.slots : n);
+  const int64_t split0 = ((int64_t)b * P.hkv + g) * P.slots;
+  const float* plse = P.part_lse + split0 * P.rows + row;
+  const float* po = P.part_o + (split0 * P.rows + row) * DV + lane * CPT;
+  const int64_t pstride = (int64_t)P.rows * DV;
+  const int nw = n > w ? (n - w + W - 1) / W : 0;  // this wave's pieces
+
+  float Mw = -INFINITY;
+  for (int t0 = 0; t0 < nw; t0 += 64) {
+    const float ls = (t0 + lane < nw) ? plse[(int64_t)(w + W * (t0 + lane)) * P.rows] : -INFINITY;
+    Mw = fmaxf(Mw, wave_max(ls));
+  }
+  float acc[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+  float Zw = 0.f;
+  for (int t0 = 0; t0 < nw; t0 += 64) {
+    const float ls = (t0 + lane < nw) ? plse[(int64_t)(w + W * (t0 + lane)) * P.rows] : -INFINITY;
+    const float wt = (ls == -INFINITY) ? 0.f : expf(ls - Mw);
+    Zw += wave_sum(wt);
+    const int cnt = min(64, nw - t0);
+    for (int s = 0; s < cnt; s += NB) {
+      Cols<CPT> vals[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (s + u < cnt) vals[u] = load_cols<CPT>(po + (int64_t)(w + W * (t0 + s + u)) * pstride);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (s + u >= cnt) break;
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), s + u));
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].v[c];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) s_acc[w][lane * CPT + c] = acc[c];
+  if (lane == 0) {
+    s_mz[w][0] = Mw;
+    s_mz[w][1] = Zw;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  // a sink joins the denominator as one more partial with a zero output
+  const float sink = P.sinks ? P.sinks[h] : -INFINITY;
+  float M = sink;
+#pragma unroll
+  for (int v = 0; v < W; ++v) M = fmaxf(M, s_mz[v][0]);
+  float Z = sink == -INFINITY ? 0.f : expf(sink - M);
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    const float f = s_mz[v][0] == -INFINITY ? 0.f : expf(s_mz[v][0] - M);
+    Z += f * s_mz[v][1];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] += f * s_acc[v][lane * CPT + c];
+  }
+  const float invZ = 1.f / Z;
+  uint16_t* op = P.out + (int64_t)r * P.o_srow + (int64_t)h * P.o_shead + lane * CPT;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) op[c] = f32_to_bf16_rne(acc[c] * invZ);
+  if (P.lse && lane == 0) P.lse[(int64_t)r * (P.hkv * P.group) + h] = M + logf(Z);
+}
+
 int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
   if (a->batch > 65535 || a->hkv > 65535) return VA_EUNSUPPORTED;
   CombineParams cp;
@@ -184,12 +273,31 @@ int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
   cp.slots = p.slots;
   cp.qo_indptr = a->qo_indptr;
   cp.sinks = a->sinks;
-  const dim3 grid((p.rows + kWaves - 1) / kWaves, a->hkv, a->batch);
+  // up to 32 slots: one wave per row; more: 4 or 16 waves share a row
+  const int wpr = p.slots > 64 ? 16 : (p.slots > 32 ? 4 : 1);
+  if (wpr == 1) {
+    const dim3 grid((p.rows + kWaves - 1) / kWaves, a->hkv, a->batch);
 #define VA_LAUNCH(DV_) \
-  return launch_kernel(reinterpret_cast<const void*>(&combine_kernel<DV_>), grid, dim3(256), cp, st)
-  if (a->v_dim == 128) VA_LAUNCH(128);
-  if (a->v_dim == 256) VA_LAUNCH(256);
-  if (a->v_dim == 512) VA_LAUNCH(512);
+    return launch_kernel(reinterpret_cast<const void*>(&combine_kernel<DV_>), grid, dim3(256), cp, st)
+    if (a->v_dim == 128) VA_LAUNCH(128);
+    if (a->v_dim == 256) VA_LAUNCH(256);
+    if (a->v_dim == 512) VA_LAUNCH(512);
+#undef VA_LAUNCH
+    return VA_EUNSUPPORTED;
+  }
+  const dim3 grid(p.rows, a->hkv, a->batch);
+#define VA_LAUNCH(DV_, W_)                                                                     \
+  return launch_kernel(reinterpret_cast<const void*>(&combine_split_kernel<DV_, W_>), grid, \
+                       dim3(64 * (W_)), cp, st)
+  if (wpr == 4) {
+    if (a->v_dim == 128) VA_LAUNCH(128, 4);
+    if (a->v_dim == 256) VA_LAUNCH(256, 4);
+    if (a->v_dim == 512) VA_LAUNCH(512, 4);
+  } else {
+    if (a->v_dim == 128) VA_LAUNCH(128, 16);
+    if (a->v_dim == 256) VA_LAUNCH(256, 16);
+    if (a->v_dim == 512) VA_LAUNCH(512, 16);
+  }
 #undef VA_LAUNCH
   return VA_EUNSUPPORTED;
 }

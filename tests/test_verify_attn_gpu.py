@@ -383,3 +383,24 @@ def test_empty_batch_and_workspace_error():
     assert B.verify_attn_fwd(call, check=False) == B.VA_EWORKSPACE
     assert B.verify_attn_combine(call, check=False) == B.VA_EWORKSPACE
     torch.cuda.synchronize()
+
+
+# A sequence spanning many pieces: the combine then merges each row with 4 or 16 waves
+# (more than 32 or 64 slots).  Explicit slot counts on one and two sequences, every
+# head width, and the split-KV page's own kernel shape (H_Q 16, H_KV 2, head_dim 256,
+# 4 drafts, batch 1) at 16k context with the heuristic's slot count.
+@pytest.mark.parametrize("dims", [0, 1, 2])
+@pytest.mark.parametrize("splits", [40, 100, 256])
+def test_combine_many_pieces(dims, splits):
+    hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
+    p = W.make_problem(name="many-pieces", batch=2, prefix_lens=[9000, 130], hq=hq, hkv=hkv,
+                       page_size=16, seed=820 + dims + splits, v_mean=1.0, **DIMS[dims])
+    check(p, num_splits=splits)
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+def test_page_kernel_shape_batch1(sinks):
+    p = W.make_problem(name="p3-b1-ctx16384", batch=1, prefix_lens=[16384], draft_len=4, hq=16,
+                       hkv=2, qk_dim=256, v_dim=256, page_size=1, seed=830 + sinks, sinks=sinks)
+    dp, _, _ = check(p)
+    assert dp.splits > 64   # the 16-wave combine
