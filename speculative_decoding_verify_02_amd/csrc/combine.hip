@@ -273,8 +273,13 @@ int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
   cp.slots = p.slots;
   cp.qo_indptr = a->qo_indptr;
   cp.sinks = a->sinks;
-  // up to 32 slots: one wave per row; more: 4 or 16 waves share a row
-  const int wpr = p.slots > 64 ? 16 : (p.slots > 32 ? 4 : 1);
+  // up to 32 slots: one wave per row; more: 4 or 16 waves share a row, while the grid
+  // stays within 16 waves per CU.  Thousands of rows fill the chip with one wave each,
+  // and there the extra waves' merge through LDS only costs time (a row's count is at
+  // most the split pass's grid height over the batch, so many rows also mean few pieces)
+  const int64_t nrows = (int64_t)a->batch * a->hkv * p.rows;
+  int wpr = p.slots > 64 ? 16 : (p.slots > 32 ? 4 : 1);
+  while (wpr > 1 && nrows * wpr > 16LL * device_cu_count()) wpr /= 4;
   if (wpr == 1) {
     const dim3 grid((p.rows + kWaves - 1) / kWaves, a->hkv, a->batch);
 #define VA_LAUNCH(DV_) \

@@ -398,6 +398,18 @@ def test_combine_many_pieces(dims, splits):
     check(p, num_splits=splits)
 
 
+# Thousands of rows with more than 64 slots: the combine keeps one wave per row there
+# (the grid already holds 16 waves per CU), so the single-wave merge runs with slot
+# counts above 64.
+@pytest.mark.parametrize("dims", [0, 1, 2])
+def test_combine_many_rows_many_slots(dims):
+    hq, hkv, batch = {0: (32, 8, 32), 1: (16, 2, 64), 2: (16, 1, 64)}[dims]
+    p = W.make_problem(name="many-rows", batch=batch, prefix_range=(40, 700), hq=hq, hkv=hkv,
+                       page_size=16, seed=840 + dims, v_mean=0.5, **DIMS[dims])
+    assert batch * hkv * (hq // hkv) * p.draft_len >= 4096
+    check(p, num_splits=100)
+
+
 @pytest.mark.parametrize("sinks", [False, True])
 def test_page_kernel_shape_batch1(sinks):
     p = W.make_problem(name="p3-b1-ctx16384", batch=1, prefix_lens=[16384], draft_len=4, hq=16,
