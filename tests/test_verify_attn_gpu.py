@@ -212,10 +212,32 @@ def test_windows(window, dims):
     check(p, num_splits=3)
 
 
-@pytest.mark.parametrize("page_size", [1, 2, 4, 8, 16, 32, 64, 128])
+@pytest.mark.parametrize("page_size", [1, 2, 4, 8, 16, 32, 64, 128, 256, 1024])
 def test_page_sizes(page_size):
     p = W.make_problem(name="pages", batch=3, prefix_lens=[129, 513, 40], hq=8, hkv=2,
                        qk_dim=128, page_size=page_size, seed=400 + page_size)
+    check(p, num_splits=2)
+
+
+# The smallest and largest page sizes on the wide-head kernels (tile, MLA): page ids
+# shifted by 0 and by 10 bits, a range that starts and ends inside one 1024-slot page.
+@pytest.mark.parametrize("dims", [1, 2])
+@pytest.mark.parametrize("page_size", [1, 1024])
+def test_page_sizes_wide_heads(dims, page_size):
+    hq, hkv = (16, 1) if DIMS[dims]["qk_dim"] == 576 else (8, 2)
+    p = W.make_problem(name="pages-wide", batch=3, prefix_lens=[1500, 700, 2100], hq=hq,
+                       hkv=hkv, page_size=page_size, seed=410 + dims + page_size, v_mean=0.5,
+                       **DIMS[dims])
+    check(p, num_splits=3)
+
+
+# The longest draft (8 tokens) on every kernel: 64 rows per KV head for the tile and MLA
+# kernels (their limit), 128 for the generic one.
+@pytest.mark.parametrize("dims,hq,hkv", [(0, 32, 2), (1, 8, 1), (2, 8, 1), (3, 16, 1)])
+def test_longest_draft_every_kernel(dims, hq, hkv):
+    p = W.make_problem(name="draft-8", batch=3, prefix_lens=[300, 0, 1200], draft_len=8, hq=hq,
+                       hkv=hkv, page_size=16, seed=420 + dims, **DIMS[dims])
+    assert (hq // hkv) * 8 <= (128 if dims in (0, 3) else 64)
     check(p, num_splits=2)
 
 
