@@ -112,9 +112,8 @@ typedef struct verify_attn_args {
     /* [B] int32 prefix lengths L_b (the KV length of sequence b is L_b + D)           */
     const int32_t* prefix_lens;
 
-    /* workspace of at least verify_attn_workspace_bytes() bytes (16-byte aligned),
-       written by verify_attn_fwd and read by verify_attn_combine; its layout is the
-       library's own (the pointer type is float only for ABI stability)                */
+    /* fp32 workspace of at least verify_attn_workspace_bytes() bytes, written by
+       verify_attn_fwd and read by verify_attn_combine                                  */
     float* workspace;
     int64_t workspace_bytes;
 
@@ -181,9 +180,8 @@ int verify_attn_build_block_table(const int32_t* kv_indptr, const int32_t* kv_in
  * range is split at sequence ends into pieces, and each piece is gathered through
  * the block table and attended by all G*D query rows of each KV head, row i
  * seeing keys p - W <= t <= p (p = L_b + i).  Piece k of sequence b writes its
- * partial output (normalised within the piece, times v_scale, rounded to bf16) and
- * its LSE (fp32) to slot k of the workspace, and the number of pieces of b is
- * recorded there too.  The
+ * partial output (normalised within the piece, times v_scale) and LSE to slot k
+ * of the workspace, and the number of pieces of b is recorded there too.  The
  * ranges are derived on the device from prefix_lens; only host scalars size the
  * grid, and a sequence never spans more than S slots.
  * Errors: VA_EINVAL / VA_EUNSUPPORTED / VA_EWORKSPACE as for can_handle plus a
@@ -225,8 +223,8 @@ int32_t verify_attn_num_splits(const verify_attn_args* args);
 
 /*
  * Workspace bytes needed for num_splits partial slots (>= 1):
- *   batch * hkv * num_splits * (hq/hkv * draft_len) * (2 * v_dim + 4) + batch * 4
- * (bf16 partial outputs, fp32 partial LSEs, one int32 piece count per sequence).
+ *   (batch * hkv * num_splits * (hq/hkv * draft_len) * (v_dim + 1) + batch) * 4
+ * (partial outputs, partial LSEs, one int32 piece count per sequence).
  * Host only.  Returns -1 on invalid input.  Size it once for the largest batch
  * and reuse it (PR #27382 review: scratch keyed on a stable max batch, fixed
  * addresses for graph replay).

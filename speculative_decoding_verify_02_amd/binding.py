@@ -341,7 +341,7 @@ def make_args(*, q, k_cache, v_cache, block_table, prefix_lens, draft_len: int, 
     q [B*D, Hq, qk_dim] bf16; k_cache [num_slots, Hkv, >= qk_dim] and v_cache
     [num_slots, Hkv, >= v_dim] (bf16, or uint8 holding e4m3fn codes) - v_cache may be
     k_cache itself (MLA alias, give v_dim); block_table [B, max_pages] int32;
-    prefix_lens [B] int32; out [B*D, Hq, v_dim] bf16; workspace a device tensor (any dtype) of
+    prefix_lens [B] int32; out [B*D, Hq, v_dim] bf16; workspace a float32 tensor of
     at least workspace_bytes() (or None while sizing it: see set_workspace); lse
     [B*D, Hq] float32 or None.  Extensions (include/verify_attn.h, version 2):
     qo_indptr [B+1] int32 (ragged rows; q/out/lse then have qo_indptr[B] rows),

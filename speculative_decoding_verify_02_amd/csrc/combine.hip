@@ -19,7 +19,7 @@
 namespace va {
 
 struct CombineParams {
-  const uint16_t* part_o;  // bf16
+  const float* part_o;
   const float* part_lse;
   const int32_t* counts;
   uint16_t* out;
@@ -51,24 +51,28 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// CPT consecutive columns of one partial row, held as loaded (bf16 pairs, half the
-// registers of fp32) and widened to fp32 where they are used.
+// CPT consecutive floats of one partial row.
 template <int CPT>
 struct Cols {
-  uint32_t w[CPT / 2];
-  __device__ __forceinline__ float at(int k) const {
-    return __uint_as_float((k & 1) ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
-  }
+  float v[CPT];
 };
 
 template <int CPT>
-__device__ __forceinline__ Cols<CPT> load_cols(const uint16_t* p) {
-  static_assert(CPT == 2 || CPT == 4 || CPT == 8, "one 4-, 8- or 16-byte load per lane");
-  typedef __attribute__((__vector_size__(CPT / 2 * sizeof(uint32_t)))) uint32_t words;
-  const words x = *reinterpret_cast<const words*>(p);
+__device__ __forceinline__ Cols<CPT> load_cols(const float* p) {
   Cols<CPT> c;
+  if constexpr (CPT % 4 == 0) {
 #pragma unroll
-  for (int k = 0; k < CPT / 2; ++k) c.w[k] = x[k];
+    for (int k = 0; k < CPT; k += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p + k);
+      c.v[k] = x[0];
+      c.v[k + 1] = x[1];
+      c.v[k + 2] = x[2];
+      c.v[k + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) c.v[k] = p[k];
+  }
   return c;
 }
 
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
   n = n < 1 ? 1 : (n > P.slots ? P.slots : n);
   const int64_t split0 = ((int64_t)b * P.hkv + g) * P.slots;
   const float* plse = P.part_lse + split0 * P.rows + row;
-  const uint16_t* po = P.part_o + (split0 * P.rows + row) * DV + lane * CPT;
+  const float* po = P.part_o + (split0 * P.rows + row) * DV + lane * CPT;
   const int64_t pstride = (int64_t)P.rows * DV;
 
   // lane s holds piece s's LSE (64 pieces per pass); the first NB pieces' columns
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
           if (s + u >= cnt) break;
           const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) acc[c] += wu * first[u].at(c);
+          for (int c = 0; c < CPT; ++c) acc[c] += wu * first[u].v[c];
         }
       } else {
         Cols<CPT> vals[NB];
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams P) {
           if (s + u >= cnt) break;
           const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].at(c);
+          for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].v[c];
         }
       }
     }
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(64 * W) void combine_split_kernel(CombineParams P) 
   n = n < 1 ? 1 : (n > P.slots ? P.slots : n);
   const int64_t split0 = ((int64_t)b * P.hkv + g) * P.slots;
   const float* plse = P.part_lse + split0 * P.rows + row;
-  const uint16_t* po = P.part_o + (split0 * P.rows + row) * DV + lane * CPT;
+  const float* po = P.part_o + (split0 * P.rows + row) * DV + lane * CPT;
   const int64_t pstride = (int64_t)P.rows * DV;
   const int nw = n > w ? (n - w + W - 1) / W : 0;  // this wave's pieces
 
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(64 * W) void combine_split_kernel(CombineParams P) 
         if (s + u >= cnt) break;
         const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), s + u));
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].at(c);
+        for (int c = 0; c < CPT; ++c) acc[c] += wu * vals[u].v[c];
       }
     }
   }
@@ -256,10 +260,9 @@ __global__ __launch_bounds__(64 * W) void combine_split_kernel(CombineParams P) 
 int launch_combine(const verify_attn_args* a, const Plan& p, hipStream_t st) {
   if (a->batch > 65535 || a->hkv > 65535) return VA_EUNSUPPORTED;
   CombineParams cp;
-  const uint8_t* ws = reinterpret_cast<const uint8_t*>(a->workspace);
-  cp.part_o = reinterpret_cast<const uint16_t*>(ws);
-  cp.part_lse = reinterpret_cast<const float*>(ws + p.ws_lse_bytes);
-  cp.counts = reinterpret_cast<const int32_t*>(ws + p.ws_cnt_bytes);
+  cp.part_o = a->workspace;
+  cp.part_lse = a->workspace + p.ws_o_floats;
+  cp.counts = reinterpret_cast<const int32_t*>(a->workspace + p.ws_cnt_floats);
   cp.out = static_cast<uint16_t*>(a->out);
   cp.o_srow = a->o_stride_row;
   cp.o_shead = a->o_stride_head;

@@ -500,7 +500,7 @@ void splitkv_fwd_kernel(FwdParams P) {
     if (row >= P.rows || row / P.group >= nrow_b) continue;
     const float l = l_run[rt];
     const float inv = l > 0.f ? P.v_scale / l : 0.f;
-    uint16_t* po = P.part_o + (split_id * P.rows + row) * DV;
+    float* po = P.part_o + (split_id * P.rows + row) * DV;
 #pragma unroll
     for (int c = 0; c < G::VG; ++c) {
 #pragma unroll
@@ -510,7 +510,7 @@ void splitkv_fwd_kernel(FwdParams P) {
           f32x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = oacc[rt][c * G::EPG + e4 + e][r] * inv;
-          store_part_bf16x4(po + c * G::CG + G::EPG * (4 * j + r) + e4, o);
+          *reinterpret_cast<f32x4*>(po + c * G::CG + G::EPG * (4 * j + r) + e4) = o;
         }
       }
     }
@@ -582,10 +582,9 @@ int launch_splitkv_fwd(const verify_attn_args* a, const Plan& p, hipStream_t st)
   fp.bt = a->block_table;
   fp.max_pages = a->max_pages_per_seq;
   fp.prefix_lens = a->prefix_lens;
-  uint8_t* ws = reinterpret_cast<uint8_t*>(a->workspace);
-  fp.part_o = reinterpret_cast<uint16_t*>(ws);
-  fp.part_lse = reinterpret_cast<float*>(ws + p.ws_lse_bytes);
-  fp.counts = reinterpret_cast<int32_t*>(ws + p.ws_cnt_bytes);
+  fp.part_o = a->workspace;
+  fp.part_lse = a->workspace + p.ws_o_floats;
+  fp.counts = reinterpret_cast<int32_t*>(a->workspace + p.ws_cnt_floats);
   fp.batch = a->batch;
   fp.hkv = a->hkv;
   fp.group = p.group;

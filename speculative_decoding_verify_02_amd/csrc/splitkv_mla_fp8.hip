@@ -585,13 +585,13 @@ __global__ __launch_bounds__(512) void splitkv_mla_fp8_kernel(FwdParams P) {
   if (rv) {
     const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
     const float inv = l_run > 0.f ? P.v_scale / (l_run * kPScale) : 0.f;
-    uint16_t* po = P.part_o + (split_id * P.rows + row) * kLat + 256 * hf + 4 * j;
+    float* po = P.part_o + (split_id * P.rows + row) * kLat + 256 * hf + 4 * j;
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
       f32x4 o = oacc[ct];
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] *= inv;
-      store_part_bf16x4(po + 16 * ct, o);
+      *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
     }
     if (hf == 0 && j == 0)
       P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;

@@ -334,13 +334,13 @@ void splitkv_tile_kernel(FwdParams P) {
     const int64_t split_id = ((int64_t)b * P.hkv + g) * P.slots + pc.slot;
     const float inv = l_run > 0.f ? P.v_scale / l_run : 0.f;
     // lane holds O[row][16ct + 4j + r], r = 0..3
-    uint16_t* po = P.part_o + (split_id * P.rows + row) * D + 4 * j;
+    float* po = P.part_o + (split_id * P.rows + row) * D + 4 * j;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       f32x4 o = oacc[ct];
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] *= inv;
-      store_part_bf16x4(po + 16 * ct, o);
+      *reinterpret_cast<f32x4*>(po + 16 * ct) = o;
     }
     if (j == 0)
       P.part_lse[split_id * P.rows + row] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;

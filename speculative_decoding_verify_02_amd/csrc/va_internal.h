@@ -37,8 +37,8 @@ struct Plan {
   int min_q;        // fewest tokens one workgroup is given
   int piece_cost;   // fixed cost of one piece, in keys of the kernel's main loop
   int max_leff;     // host bound of the attended prefix length
-  int64_t ws_lse_bytes;  // offset of the partial LSEs in the workspace (after the bf16 outputs)
-  int64_t ws_cnt_bytes;  // offset of the per-sequence piece counts (int32)
+  int64_t ws_o_floats;    // offset of partial LSEs in the workspace (floats)
+  int64_t ws_cnt_floats;  // offset of the per-sequence piece counts (int32)
 };
 
 // Split-KV kernel parameters (strides in bytes), resolved from verify_attn_args.
@@ -52,7 +52,7 @@ struct FwdParams {
   const int32_t* bt;
   int32_t max_pages;
   const int32_t* prefix_lens;
-  uint16_t* part_o;  // bf16 partial outputs
+  float* part_o;
   float* part_lse;
   int32_t* counts;   // [B] pieces written per sequence
   int batch, hkv, group, draft, rows, lg_page, window;
@@ -66,15 +66,6 @@ struct FwdParams {
   const uint8_t* tree_mask;    // [B, D, D] tree verify: row i sees draft key j
   float logit_cap;             // > 0: natural-log scores s -> cap * tanh(s / cap)
 };
-
-// Four consecutive columns of a partial output row as bf16 (round to nearest even), one
-// 8-byte store.  The partial is the piece's normalised output, merged in fp32 by the
-// combine; bf16 halves the bytes written here and read back there.
-__device__ __forceinline__ void store_part_bf16x4(uint16_t* p, f32x4 o) {
-  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-  const bf16x4 v = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-  *reinterpret_cast<bf16x4*>(p) = v;
-}
 
 // Read-only int32 tables (prefix lengths, row offsets, block table) through the constant address
 // space: a wave-uniform index then becomes a scalar load.

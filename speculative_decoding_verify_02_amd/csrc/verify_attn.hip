@@ -196,11 +196,8 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
   // one slot: grid row y takes all of sequence y
   p->nwy = p->slots == 1 ? (a->batch > 0 ? a->batch : 1) : nwy;
   if (p->nwy > 65535) return VA_EUNSUPPORTED;
-  // workspace: bf16 partial outputs [B, hkv, S, rows, v_dim], fp32 partial LSEs
-  // [B, hkv, S, rows], int32 piece counts [B]
-  const int64_t nparts = (int64_t)a->batch * a->hkv * p->slots * rows;
-  p->ws_lse_bytes = nparts * a->v_dim * 2;
-  p->ws_cnt_bytes = p->ws_lse_bytes + nparts * 4;
+  p->ws_o_floats = (int64_t)a->batch * a->hkv * p->slots * rows * a->v_dim;
+  p->ws_cnt_floats = p->ws_o_floats + (int64_t)a->batch * a->hkv * p->slots * rows;
   return VA_OK;
 }
 
@@ -253,7 +250,7 @@ int64_t verify_attn_workspace_bytes(int32_t batch, int32_t hkv, int32_t hq, int3
   if (batch < 0 || hkv < 1 || hq < 1 || hq % hkv || draft_len < 1 || v_dim < 1 || num_splits < 1)
     return -1;
   const int64_t rows = (int64_t)(hq / hkv) * draft_len;
-  return (int64_t)batch * hkv * num_splits * rows * (2 * (int64_t)v_dim + 4) + (int64_t)batch * 4;
+  return ((int64_t)batch * hkv * num_splits * rows * ((int64_t)v_dim + 1) + batch) * 4;
 }
 
 // Copies the caller's arguments into a full current-version struct: a version 1

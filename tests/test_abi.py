@@ -150,7 +150,7 @@ def test_noalloc_rejects_before_any_launch():
     assert noalloc(draft_len=9) == B.VA_EUNSUPPORTED
     assert noalloc(batch=0, workspace=None, workspace_bytes=0) == B.VA_OK
     # partials beyond the static array: an explicit slot count that does not fit, and a
-    # batch for which not even one slot per sequence fits (2000 x 64 rows x 1028 B)
+    # batch for which not even one slot per sequence fits (2000 x 2 x 16 rows x 513 x 4 B)
     per_slot = B.verify_attn_workspace_bytes(2, 2, 8, 4, 128, 1) - 2 * 4
     fit = (B.STATIC_SCRATCH_BYTES - 8) // per_slot
     assert noalloc(num_splits=fit + 1) == B.VA_EWORKSPACE
@@ -161,8 +161,7 @@ def test_noalloc_rejects_before_any_launch():
 
 def test_workspace_checked_before_launch():
     need = B.verify_attn_workspace_bytes(2, 2, 8, 4, 128, 4)
-    # bf16 partial outputs and fp32 LSEs, then one piece count per sequence
-    assert need == 2 * 2 * 4 * 16 * (2 * 128 + 4) + 2 * 4
+    assert need == (2 * 2 * 4 * 16 * 129 + 2) * 4     # partials + one piece count per sequence
     assert fwd(workspace_bytes=need - 1) == B.VA_EWORKSPACE
     assert combine(workspace_bytes=need - 1) == B.VA_EWORKSPACE
 
