@@ -17,7 +17,9 @@ from dataclasses import dataclass
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libverify_attn.so")
+# the in-tree build; VERIFY_ATTN_LIB names another build of the same sources (the
+# host-sanitizer build the CPU tests load, for instance)
+LIB_PATH = os.environ.get("VERIFY_ATTN_LIB") or os.path.join(PKG, "libverify_attn.so")
 
 VA_OK, VA_EINVAL, VA_EUNSUPPORTED, VA_EWORKSPACE, VA_EHIP = 0, 1, 2, 3, 4
 VA_KV_BF16, VA_KV_FP8_E4M3FN = 0, 1

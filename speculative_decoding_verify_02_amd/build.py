@@ -11,6 +11,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -51,6 +52,50 @@ def _run(cmd: list, verbose: bool) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+
+
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests of
+# the C ABI (which never reach a kernel launch).  Every sanitizer flag applies to the
+# host side only; the device code is built as usual.
+HOST_SANITIZER_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split() + [
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> Optional[str]:
+    """The compiler's shared AddressSanitizer runtime (it carries the UBSan handlers too),
+    to preload into a process that loads the sanitized library; None if absent."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")) +
+                  glob.glob(os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_host_sanitized(out_path: str, extra_sources=(), verbose: bool = False) -> str:
+    """Compile the library's host-side sources (argument checks, planning, workspace
+    sizing, the block-table and combine launchers) with their host code under ASan +
+    UBSan into out_path, together with `extra_sources` (the caller's stand-in for the
+    split-KV launcher, whose kernels such a build leaves out).  Load it with
+    sanitizer_runtime() preloaded."""
+    sources = [os.path.join(CSRC, s) for s in ("verify_attn.hip", "block_table.hip", "combine.hip")]
+    sources += list(extra_sources)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + ["-Xarch_host", "-g"]
+    objdir = tempfile.mkdtemp(prefix="va_hostsan_")
+    try:
+        objs = [os.path.join(objdir, f"{i}.o") for i in range(len(sources))]
+        cmds = [[hipcc(), *flags, *HOST_SANITIZER_FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, s, "-o", o]
+                for s, o in zip(sources, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SANITIZER_FLAGS, *objs,
+              "-o", out_path], verbose)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    return out_path
 
 
 def build(verbose: bool = False) -> str:
