@@ -98,6 +98,10 @@ struct KVRegs {
 // same slot order, which is all the MFMA reduction needs.
 __device__ __forceinline__ int slot_token(int j, int i) { return 16 * (i >> 2) + 4 * j + (i & 3); }
 
+// The K and V rows are read once per call: non-temporal loads, so the stream does not
+// displace what is reused (page ids, q, the partials the combine reads back) from the
+// L2s and the Infinity Cache.  On the long-context batch this took the pass from 397 to
+// 357 us; making the partial stores non-temporal as well cost 50 us.
 template <class G>
 __device__ __forceinline__ void load_block(KVRegs<G>& R, int lslot, const uint8_t* kg,
                                            const uint8_t* vg, uint32_t k_sslot, uint32_t v_sslot,
@@ -106,7 +110,8 @@ __device__ __forceinline__ void load_block(KVRegs<G>& R, int lslot, const uint8_
   for (int u = 0; u < G::NKLD; ++u) {
     const int q = 64 * u + lane;
     const int sl = __shfl(lslot, q / G::KCH, 64);
-    R.k[u] = *reinterpret_cast<const u32x4*>(kg + (uint64_t)(uint32_t)sl * k_sslot + 16 * (q % G::KCH));
+    R.k[u] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(kg + (uint64_t)(uint32_t)sl * k_sslot + 16 * (q % G::KCH)));
   }
 #pragma unroll
   for (int i = 0; i < 4 * G::TB / 16; ++i) {
@@ -115,13 +120,13 @@ __device__ __forceinline__ void load_block(KVRegs<G>& R, int lslot, const uint8_
 #pragma unroll
     for (int c = 0; c < G::VG; ++c) {
       if constexpr (G::VGB == 16) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vp + 256 * c);
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 256 * c));
         R.v[i][4 * c + 0] = x[0];
         R.v[i][4 * c + 1] = x[1];
         R.v[i][4 * c + 2] = x[2];
         R.v[i][4 * c + 3] = x[3];
       } else {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp));
         R.v[i][0] = x[0];
         R.v[i][1] = x[1];
       }

@@ -108,7 +108,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Copies to LDS at `lds` + lane * 16 straight from global memory.  Inline assembly,
 // so the compiler (which does not see these copies) adds no waits of its own before
 // LDS reads; the waits are explicit.  M0 holds the wave's LDS base and needs one
-// wait state before the copy reads it.
+// wait state before the copy reads it.  (Non-temporal copies, `nt`, left this compute-
+// bound pass's time unchanged and raised its fetched bytes by 19 MB per call.)
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds) : "memory", "m0");

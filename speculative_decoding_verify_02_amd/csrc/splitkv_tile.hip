@@ -201,8 +201,11 @@ void splitkv_tile_kernel(FwdParams P) {
       } else {
         slot = __shfl(sl_lane, (64 * G::W * u + tid) / G::CH, 64);
       }
-      kr[set][u] = *reinterpret_cast<const u32x4*>(P.k + (uint64_t)slot * k_sslot + koff[u]);
-      vr[set][u] = *reinterpret_cast<const u32x4*>(P.v + (uint64_t)slot * v_sslot + voff[u]);
+      // read once: non-temporal, so the stream leaves the reused data in the caches
+      kr[set][u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(P.k + (uint64_t)slot * k_sslot + koff[u]));
+      vr[set][u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(P.v + (uint64_t)slot * v_sslot + voff[u]));
     }
   };
   auto load = [&](auto set, int sl_lane) { load_part(set, sl_lane, 0, G::NLD); };
