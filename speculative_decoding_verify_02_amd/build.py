@@ -98,6 +98,25 @@ def build_host_sanitized(out_path: str, extra_sources=(), verbose: bool = False)
     return out_path
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "verify_c_caller.c")
+C_CALLER_PATH = os.path.join(ROOT, "tests", "c_abi", "verify_c_caller")
+
+
+def build_c_caller(out_path: str = C_CALLER_PATH, verbose: bool = False) -> str:
+    """Compile the plain C caller of the library (tests/c_abi/verify_c_caller.c) with the
+    host C compiler against include/verify_attn.h, the in-tree library and the HIP
+    runtime's C API.  Returns the executable's path."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler")
+    _run([cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CALLER_SRC,
+          "-L", PKG, "-lverify_attn", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+          f"-Wl,-rpath,{PKG}:{os.path.join(rocm, 'lib')}", "-o", out_path], verbose)
+    return out_path
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into LIB_PATH (always recompiles).  Returns the path.
 
