@@ -173,9 +173,14 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
     p->nrg = groups <= 1 ? 1 : (groups <= 2 ? 2 : (groups <= 4 ? 4 : 0));
     if (p->nrg == 0) return VA_EUNSUPPORTED;
     // the remaining waves of a workgroup cover more KV heads of the same tokens, then
-    // interleave tokens of one head
+    // interleave tokens of one head.  bf16 d = 128 takes at most 2 heads (so 2 token
+    // lanes each): against 4 heads, with the non-temporal KV loads, the long-context
+    // batch went 358.8 -> 344.6 us, with a 4096-key window 97.0 -> 87.1 us, 4 KV heads
+    // 196 -> 186.6 us and the Llama-8B shape 17.7 -> 14.8 us; fp8 d = 128 keeps 4
+    // (206 us against 212 at 2)
     const int free_waves = kWaves / p->nrg;
-    p->hpc = a->hkv >= free_waves ? free_waves : (a->hkv >= 2 && free_waves >= 2 ? 2 : 1);
+    const int cap = (!fp8 && a->qk_dim == 128 && free_waves > 2) ? 2 : free_waves;
+    p->hpc = a->hkv >= cap ? cap : (a->hkv >= 2 && cap >= 2 ? 2 : 1);
     p->ntl = free_waves / p->hpc;
     head_groups = (a->hkv + p->hpc - 1) / p->hpc;
     per_cu = (a->qk_dim == 128 && p->rt == 1) ? 2 : 1;
