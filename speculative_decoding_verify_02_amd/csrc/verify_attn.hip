@@ -183,7 +183,11 @@ int make_plan(const verify_attn_args* a, Plan* p, bool check_pointers) {
     p->hpc = a->hkv >= cap ? cap : (a->hkv >= 2 && cap >= 2 ? 2 : 1);
     p->ntl = free_waves / p->hpc;
     head_groups = (a->hkv + p->hpc - 1) / p->hpc;
-    per_cu = (a->qk_dim == 128 && p->rt == 1) ? 2 : 1;
+    // fp8 d = 128 with one row tile: two workgroups per CU; bf16 d = 128 one (with two
+    // heads per workgroup that beat two per CU: long-context batch 344.0 -> 336.3 us,
+    // Llama-8B shape call 23.4 -> 20.4 us, window 87.5 -> 85.2 us; fp8 at one per CU
+    // 208 -> 285 us)
+    per_cu = (a->qk_dim == 128 && p->rt == 1 && fp8) ? 2 : 1;
   }
   p->hg = head_groups;
   p->lg_page = ilog2(a->page_size);
